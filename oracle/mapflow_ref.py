@@ -1,0 +1,229 @@
+"""fp64 reference of MapFlow's compression and fused retrieval (test infrastructure).
+
+Notation: N tokens, block size B, T = ceil(N / B) block rows and columns,
+H_s sender heads, H_r receiver heads, H_kv receiver KV heads with
+G = H_r / H_kv receiver heads per KV head, d head dimension.
+
+  A[h][i][j]        causal sender attention map of one sender layer
+  mass[I][J]        head-averaged block mass (J <= I; zero above the diagonal)
+  row_ptr[T+1], col_idx[nnzb], vals[nnzb][H_s][B][B]   Block Sparse Row state
+  W[H_r][H_s]       learned head map of one reuse receiver layer
+  V[N][H_kv][d]     receiver values;  O[N][H_r][d] attention output
+
+Each step has a per-block-row function (``*_row``) and a whole-map wrapper
+that loops over the rows.  ``A`` only needs ``.shape`` and basic slicing that
+returns something ``np.asarray`` accepts, so a test can hand in a lazy view of
+a map that lives elsewhere and check sampled block rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def n_blocks(N: int, B: int) -> int:
+    return -(-N // B)
+
+
+def _span(X: int, B: int, N: int) -> tuple[int, int]:
+    return X * B, min(N, (X + 1) * B)
+
+
+# ---------------------------------------------------------------------------
+# 1. block statistics
+# ---------------------------------------------------------------------------
+
+def block_mass_row(A, B: int, I: int) -> np.ndarray:
+    """mass[I][0..I] of one block row, fp64.
+
+    MapFlow's compressor first computes a statistic per block and then chooses
+    blocks (article aitest123.com/news/zaoi86, third section, first component);
+    the selection threshold is a cumulative attention probability (paper page,
+    highlight 3).  The statistic is therefore the attention probability that
+    falls in the block: the plain sum of A over the block's rows and columns,
+    averaged over the sender heads with equal weight, because one cached sender
+    state serves receivers with different head maps (article, third section,
+    second component).  Rows and columns at or beyond N do not exist (partial
+    last block).  Only causal blocks J <= I are candidates.
+    """
+    H, N, _ = A.shape
+    r0, r1 = _span(I, B, N)
+    slab = np.asarray(A[:, r0:r1, : min(N, (I + 1) * B)], dtype=F64)
+    out = np.zeros(I + 1, dtype=F64)
+    for J in range(I + 1):
+        c0, c1 = _span(J, B, N)
+        out[J] = slab[:, :, c0:c1].sum() / H
+    return out
+
+
+def block_mass(A, B: int) -> np.ndarray:
+    """mass[T][T] fp64 for the whole map (zeros above the diagonal)."""
+    H, N, N2 = A.shape
+    assert N == N2
+    T = n_blocks(N, B)
+    mass = np.zeros((T, T), dtype=F64)
+    for I in range(T):
+        mass[I, : I + 1] = block_mass_row(A, B, I)
+    return mass
+
+
+# ---------------------------------------------------------------------------
+# 2. block-level Top-p
+# ---------------------------------------------------------------------------
+
+def topp_row(m, p: float) -> np.ndarray:
+    """Kept columns (ascending) of one block row with candidate masses m[0..I].
+
+    Block-level Top-p (paper page, highlight 3): candidates are visited in
+    order of decreasing mass (equal masses: lower column first); blocks are
+    kept until the kept mass first reaches p times the row's total mass
+    (inclusive: the block that reaches it is kept).  p >= 1 keeps every causal
+    block.  Nothing is renormalised; dropped mass is lost.  Sums run in fp64:
+    the total in column order, the running sum in visiting order.
+    """
+    m = [float(x) for x in np.asarray(m, dtype=F64)]
+    n = len(m)
+    p = float(np.float32(p))          # the boundary passes p as fp32
+    if p >= 1.0:
+        return np.arange(n, dtype=np.int64)
+    total = 0.0
+    for x in m:
+        total += x
+    threshold = p * total
+    order = sorted(range(n), key=lambda J: (-m[J], J))
+    cum = 0.0
+    chosen = []
+    for J in order:
+        chosen.append(J)
+        cum += m[J]
+        if cum >= threshold:
+            break
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
+def decision_masses(mass) -> np.ndarray:
+    """Masses as the selection sees them.  The library stores block masses as
+    fp32 and takes the Top-p decision on those values, so the decision is
+    taken here on the fp64 masses rounded once to fp32 (then widened back)."""
+    return np.asarray(mass, dtype=F64).astype(np.float32).astype(F64)
+
+
+def topp_select(mass, p: float) -> list:
+    """Per-row kept columns for a [T][T] mass matrix (decision on fp32 masses)."""
+    m32 = decision_masses(mass)
+    return [topp_row(m32[I, : I + 1], p) for I in range(m32.shape[0])]
+
+
+# ---------------------------------------------------------------------------
+# 3. Block Sparse Row state
+# ---------------------------------------------------------------------------
+
+def bsr_tile(A, B: int, I: int, J: int) -> np.ndarray:
+    """vals entry of block (I, J): the [H_s][B][B] tile copied exactly in the
+    input dtype, zeros for rows or columns at or beyond N (paper page,
+    "Practical Implementation Details": BSR with regular 2-D blocks)."""
+    H, N, _ = A.shape
+    r0, r1 = _span(I, B, N)
+    c0, c1 = _span(J, B, N)
+    src = np.asarray(A[:, r0:r1, c0:c1])
+    tile = np.zeros((H, B, B), dtype=src.dtype)
+    tile[:, : r1 - r0, : c1 - c0] = src
+    return tile
+
+
+def build_bsr(A, B: int, kept: list):
+    """row_ptr[T+1], col_idx[nnzb], vals[nnzb][H_s][B][B] of the kept blocks.
+    All H_s heads share one pattern; col_idx is ascending within a row."""
+    H, N, _ = A.shape
+    T = n_blocks(N, B)
+    assert len(kept) == T
+    counts = np.array([len(k) for k in kept], dtype=np.int64)
+    row_ptr = np.zeros(T + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    nnzb = int(row_ptr[-1])
+    col_idx = (np.concatenate([np.asarray(k, dtype=np.int64) for k in kept])
+               if nnzb else np.zeros(0, dtype=np.int64))
+    dtype = np.asarray(A[:1, :1, :1]).dtype
+    vals = np.zeros((nnzb, H, B, B), dtype=dtype)
+    k = 0
+    for I in range(T):
+        for J in kept[I]:
+            vals[k] = bsr_tile(A, B, I, int(J))
+            k += 1
+    return row_ptr, col_idx, vals
+
+
+# ---------------------------------------------------------------------------
+# 4. fused head-mapped retrieval
+# ---------------------------------------------------------------------------
+
+def retrieve_row(I: int, cols, tiles, W, V, N: int, B: int) -> np.ndarray:
+    """O rows of block row I, [rows][H_r][d] fp64, from its kept blocks.
+
+    For a reuse receiver layer, receiver head r's map is a linear combination
+    of the sender heads with the learned weights W[r][:] (paper page, "MapFlow
+    System Design" item 3 and highlight 2; article, second section: a learned
+    linear combination of heads).  The kernel the pages describe reads only the
+    kept blocks, mixes heads on chip and multiplies by the receiver's own
+    values, accumulating the output (article, third section, third component;
+    paper page, highlight 4).  Per kept block (I, J) and receiver head r:
+
+        Ahat[r] = sum_s W[r][s] * tile[s]                      (B x B)
+        O[I*B + i][r][:] += sum_c Ahat[r][i][c] * V[J*B + c][g(r)][:]
+
+    with g(r) = r // (H_r / H_kv): consecutive receiver heads share a KV head.
+    Rows and columns at or beyond N are skipped.  No bias, no renormalisation.
+    """
+    W64 = np.asarray(W, dtype=F64)
+    H_r, H_s = W64.shape
+    V = np.asarray(V)
+    H_kv, d = V.shape[1], V.shape[2]
+    assert H_r % H_kv == 0
+    G = H_r // H_kv
+    r0, r1 = _span(I, B, N)
+    O = np.zeros((r1 - r0, H_r, d), dtype=F64)
+    for J, tile in zip(cols, tiles):
+        c0, c1 = _span(int(J), B, N)
+        blk = np.asarray(tile, dtype=F64)                  # [H_s][B][B]
+        Vblk = np.asarray(V[c0:c1], dtype=F64)             # [cols][H_kv][d]
+        for r in range(H_r):
+            ahat = np.zeros((B, B), dtype=F64)
+            for s in range(H_s):
+                ahat += W64[r, s] * blk[s]
+            O[:, r, :] += ahat[: r1 - r0, : c1 - c0] @ Vblk[:, r // G, :]
+    return O
+
+
+def retrieve(row_ptr, col_idx, vals, W, V, N: int, B: int) -> np.ndarray:
+    """O[N][H_r][d] fp64 for a whole BSR state (loops retrieve_row)."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    T = len(row_ptr) - 1
+    assert T == n_blocks(N, B)
+    H_r = np.asarray(W).shape[0]
+    d = np.asarray(V).shape[2]
+    O = np.zeros((N, H_r, d), dtype=F64)
+    for I in range(T):
+        k0, k1 = int(row_ptr[I]), int(row_ptr[I + 1])
+        r0, r1 = _span(I, B, N)
+        O[r0:r1] = retrieve_row(I, col_idx[k0:k1], vals[k0:k1], W, V, N, B)
+    return O
+
+
+def compress(A, B: int, p: float):
+    """Sender-side compression: block mass -> Top-p -> BSR.
+    Returns (mass, kept, row_ptr, col_idx, vals)."""
+    mass = block_mass(A, B)
+    kept = topp_select(mass, p)
+    row_ptr, col_idx, vals = build_bsr(A, B, kept)
+    return mass, kept, row_ptr, col_idx, vals
+
+
+def pipeline_row(A, V, W, B: int, p: float, I: int):
+    """Everything for one block row: (mass row, kept columns, tiles, O rows)."""
+    N = A.shape[1]
+    m = block_mass_row(A, B, I)
+    kept = topp_row(decision_masses(m), p)
+    tiles = [bsr_tile(A, B, I, int(J)) for J in kept]
+    O = retrieve_row(I, kept, tiles, W, V, N, B)
+    return m, kept, tiles, O

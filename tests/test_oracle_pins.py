@@ -1,0 +1,360 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test ties an oracle step to an independent fact: a library routine
+(torch SDPA, scipy.sparse BSR), brute force, a closed form, an invariant of
+the Top-p rule, or a hand-worked example.  Together they catch a dropped term,
+a wrong sign or index and a transposed operand anywhere in the oracle.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.sparse as sp
+import torch
+
+import oracle
+import synth
+from tests._compare import check_bsr_structure, selection_ok
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _dense_from_bsr(row_ptr, col_idx, vals, N, B):
+    """Scatter a BSR state to a dense [H_s][N][N] map (test-side brute force)."""
+    H = vals.shape[1]
+    T = len(row_ptr) - 1
+    D = np.zeros((H, T * B, T * B))
+    for I in range(T):
+        for k in range(row_ptr[I], row_ptr[I + 1]):
+            J = col_idx[k]
+            D[:, I * B:(I + 1) * B, J * B:(J + 1) * B] = vals[k]
+    return D[:, :N, :N]
+
+
+def _dense_retrieval(A_dense, W, V):
+    """O = (W (x) A) V over the full dense map, one receiver head at a time."""
+    H_r = W.shape[0]
+    H_kv = V.shape[1]
+    G = H_r // H_kv
+    N = A_dense.shape[1]
+    O = np.zeros((N, H_r, V.shape[2]))
+    for r in range(H_r):
+        Ahat = np.tensordot(W[r], A_dense, axes=(0, 0))     # [N][N]
+        O[:, r, :] = Ahat @ V[:, r // G, :]
+    return O
+
+
+def _random_causal_map(rng, H, N, dirichlet=False):
+    A = rng.random((H, N, N)) ** 3
+    A *= np.tril(np.ones((N, N)))[None]
+    A /= A.sum(-1, keepdims=True)
+    return A
+
+
+# ---- P1: identity -> dense causal attention (torch SDPA) -------------------
+
+@pytest.mark.parametrize("N,B", [(256, 16), (250, 16), (100, 32)])
+def test_identity_reproduces_dense_attention_fp64(N, B):
+    w = synth.workload("tiny-f32", N=N, B=B)
+    L = synth.gen_layer(w, map_dtype="f64", return_qk=True)
+    A = L["A"].numpy()
+    V = L["V"].double().numpy()
+    W = np.eye(w.H_s)
+    _, kept, rp, ci, vals = oracle.compress(A, B, 1.0)
+    assert rp[-1] == w.T * (w.T + 1) // 2
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    q, k = L["Q"], L["K"]                                # [H][N][d] fp64
+    v = torch.from_numpy(V).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    ref = ref.permute(1, 0, 2).numpy()
+    err = np.abs(O - ref).max() / np.abs(ref).max()
+    assert err < 1e-12, err
+
+
+def test_identity_with_fp32_maps_within_fp32_bar():
+    w = synth.workload("tiny-f32")
+    L = synth.gen_layer(w, return_qk=True)               # maps stored fp32
+    A = L["A"].numpy()
+    V = L["V"].double().numpy()
+    _, _, rp, ci, vals = oracle.compress(A, w.B, 1.0)
+    O = oracle.retrieve(rp, ci, vals, np.eye(w.H_s), V, w.N, w.B)
+    v = torch.from_numpy(V).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(L["Q"], L["K"], v, is_causal=True)
+    ref = ref.permute(1, 0, 2).numpy()
+    assert np.abs(O - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+# ---- P2: brute-force decompress-then-matmul, scipy BSR ---------------------
+
+@pytest.mark.parametrize("N,B,H_s,H_r,H_kv,d,p", [
+    (100, 16, 3, 6, 2, 8, 0.7),
+    (64, 16, 4, 4, 4, 5, 0.9),
+    (37, 32, 2, 3, 1, 4, 0.5),
+])
+def test_retrieval_matches_dense_brute_force(N, B, H_s, H_r, H_kv, d, p):
+    rng = np.random.default_rng(N * 7 + H_s)
+    A = _random_causal_map(rng, H_s, N)
+    W = rng.standard_normal((H_r, H_s))
+    V = rng.standard_normal((N, H_kv, d))
+    _, kept, rp, ci, vals = oracle.compress(A, B, p)
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    ref = _dense_retrieval(_dense_from_bsr(rp, ci, vals, N, B), W, V)
+    assert np.abs(O - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_retrieval_matches_scipy_bsr_for_one_hot_head_map():
+    rng = np.random.default_rng(3)
+    N, B, H_s = 96, 16, 3
+    A = _random_causal_map(rng, H_s, N)
+    V = rng.standard_normal((N, 1, 6))
+    _, _, rp, ci, vals = oracle.compress(A, B, 0.8)
+    for s0 in range(H_s):
+        W = np.zeros((1, H_s))
+        W[0, s0] = 1.0
+        O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+        M = sp.bsr_matrix((vals[:, s0], ci, rp), shape=(N, N))
+        ref = M @ V[:, 0, :]
+        assert np.abs(O[:, 0, :] - ref).max() < 1e-12
+
+
+def test_retrieval_of_arbitrary_pattern_matches_brute_force():
+    """Retrieval must not rely on the pattern being a Top-p pattern."""
+    rng = np.random.default_rng(11)
+    N, B, H_s, H_r, H_kv, d = 70, 16, 3, 4, 2, 3
+    T = oracle.n_blocks(N, B)
+    A = rng.standard_normal((H_s, N, N))          # not even a probability map
+    kept = [np.sort(rng.choice(I + 1, size=rng.integers(0, I + 2), replace=False))
+            for I in range(T)]
+    rp, ci, vals = oracle.build_bsr(A, B, kept)
+    W = rng.standard_normal((H_r, H_s))
+    V = rng.standard_normal((N, H_kv, d))
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    ref = _dense_retrieval(_dense_from_bsr(rp, ci, vals, N, B), W, V)
+    assert np.abs(O - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# ---- P3/P4/P5: Top-p invariants, brute force, monotonicity, extremes -------
+
+def _brute_force_topp(m, p):
+    """Smallest subset reaching p*total; among those, the heaviest (exhaustive)."""
+    n = len(m)
+    tot = float(np.sum(m))
+    thr = float(np.float32(p)) * tot
+    for size in range(1, n + 1):
+        best = None
+        for sub in itertools.combinations(range(n), size):
+            s = sum(m[j] for j in sub)
+            if s >= thr * (1 - 1e-12) and (best is None or s > best[0]):
+                best = (s, sub)
+        if best is not None:
+            return size, best[0]
+    return n, tot
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topp_matches_exhaustive_search(seed):
+    rng = np.random.default_rng(seed)
+    for n in range(1, 11):
+        m = rng.random(n) ** 4
+        for p in (0.3, 0.6, 0.9, 0.99):
+            kept = oracle.topp_row(m, p)
+            size, best = _brute_force_topp(m, p)
+            assert len(kept) == size, (m, p, kept)
+            assert abs(sum(m[j] for j in kept) - best) <= 1e-12
+
+
+@pytest.mark.parametrize("p", [0.5, 0.8, 0.9, 0.95, 0.999])
+def test_topp_invariants_on_maps(p):
+    w = synth.workload("pair14b8b-bf16", N=640, H_s=4)
+    A = synth.gen_layer(w)["A"].float().numpy()
+    mass = oracle.block_mass(A, w.B)
+    kept = oracle.topp_select(mass, p)
+    T = w.T
+    rp, ci, vals = oracle.build_bsr(A, w.B, kept)
+    check_bsr_structure(rp, ci, T)
+    m32 = oracle.decision_masses(mass)
+    for I in range(T):
+        m = m32[I, : I + 1]
+        S = set(kept[I].tolist())
+        ks = np.array([m[j] for j in S])
+        tot = m.sum()
+        assert ks.sum() >= float(np.float32(p)) * tot * (1 - 1e-12)
+        assert ks.sum() - ks.min() < float(np.float32(p)) * tot      # minimal
+        dropped = [m[j] for j in range(I + 1) if j not in S]
+        if dropped:
+            assert ks.min() >= max(dropped)                          # heaviest kept
+        assert selection_ok(mass[I, : I + 1], kept[I], kept[I], p) == "exact"
+
+
+def test_topp_monotone_in_p():
+    rng = np.random.default_rng(5)
+    T = 24
+    mass = np.tril(rng.random((T, T)) ** 3)
+    prev = None
+    nn_prev = 0
+    for p in (0.1, 0.5, 0.8, 0.9, 0.95, 1.0):
+        kept = oracle.topp_select(mass, p)
+        nn = sum(len(k) for k in kept)
+        assert nn >= nn_prev
+        if prev is not None:
+            for a, b in zip(prev, kept):
+                assert set(a.tolist()) <= set(b.tolist())
+        prev, nn_prev = kept, nn
+
+
+def test_topp_extremes_and_ties():
+    m = np.array([0.2, 0.5, 0.5, 0.1])
+    assert oracle.topp_row(m, 1.0).tolist() == [0, 1, 2, 3]
+    assert oracle.topp_row(m, 1e-9).tolist() == [1]        # arg-max, tie -> lower J
+    assert oracle.topp_row(m, 0.38).tolist() == [1]        # 0.5 >= 0.38*1.3 = 0.494
+    assert oracle.topp_row(m, 0.4).tolist() == [1, 2]      # 0.52 needs the tied block 2
+    assert oracle.topp_row(np.zeros(5), 0.9).tolist() == [0]  # zero row: first block
+    T = 9
+    mass = np.tril(np.ones((T, T)))
+    kept = oracle.topp_select(mass, 1.0)
+    assert sum(len(k) for k in kept) == T * (T + 1) // 2
+    kept = oracle.topp_select(mass, 1e-7)
+    assert all(k.tolist() == [0] for k in kept)           # all tied -> column 0
+
+
+# ---- P6: block-mass identities and a closed form ---------------------------
+
+@pytest.mark.parametrize("N,B", [(256, 16), (250, 16), (97, 32)])
+def test_block_mass_rows_sum_to_valid_row_count(N, B):
+    w = synth.workload("tiny-f32", N=N, B=B)
+    A = synth.gen_layer(w, map_dtype="f64")["A"].numpy()
+    mass = oracle.block_mass(A, B)
+    T = w.T
+    for I in range(T):
+        rows = min(N, (I + 1) * B) - I * B
+        assert abs(mass[I].sum() - rows) < 1e-12
+        assert (mass[I, I + 1:] == 0).all()
+
+
+def test_block_mass_closed_form_uniform_attention():
+    """A[h][i][j] = 1/(i+1) for j <= i: mass[I][J] = sum_i |J cap [0,i]| / (i+1)."""
+    N, B, H = 23, 4, 3
+    A = np.zeros((H, N, N))
+    for i in range(N):
+        A[:, i, : i + 1] = 1.0 / (i + 1)
+    A[1] *= 2.0                                # heads weigh equally in the average
+    A[2] *= 0.5
+    mass = oracle.block_mass(A, B)
+    T = oracle.n_blocks(N, B)
+    scale = (1.0 + 2.0 + 0.5) / 3
+    for I in range(T):
+        for J in range(T):
+            expect = 0.0
+            if J <= I:
+                for i in range(I * B, min(N, (I + 1) * B)):
+                    lo, hi = J * B, min(N, (J + 1) * B, i + 1)
+                    expect += max(0, hi - lo) / (i + 1)
+            assert abs(mass[I, J] - scale * expect) < 1e-12, (I, J)
+
+
+# ---- P7: algebra of the retrieval ------------------------------------------
+
+def test_retrieval_algebra():
+    rng = np.random.default_rng(9)
+    N, B, H_s, H_r, H_kv, d = 80, 16, 3, 4, 2, 5
+    A = _random_causal_map(rng, H_s, N)
+    _, _, rp, ci, vals = oracle.compress(A, B, 0.85)
+    W1, W2 = rng.standard_normal((2, H_r, H_s))
+    V1, V2 = rng.standard_normal((2, N, H_kv, d))
+    R = lambda W, V: oracle.retrieve(rp, ci, vals, W, V, N, B)
+    assert np.abs(R(np.zeros((H_r, H_s)), V1)).max() == 0.0
+    assert np.abs(R(W1 + W2, V1) - R(W1, V1) - R(W2, V1)).max() < 1e-12
+    assert np.abs(R(W1, V1 + 2 * V2) - R(W1, V1) - 2 * R(W1, V2)).max() < 1e-12
+    # swapping two receiver heads of one KV group swaps their outputs
+    Wp = W1.copy()
+    Wp[[0, 1]] = Wp[[1, 0]]
+    assert np.abs(R(Wp, V1)[:, [1, 0]] - R(W1, V1)[:, [0, 1]]).max() < 1e-12
+
+
+def test_single_block_is_a_dense_matmul():
+    rng = np.random.default_rng(4)
+    N, B, H_r, d = 13, 16, 3, 4
+    A = _random_causal_map(rng, 1, N)
+    W = rng.standard_normal((H_r, 1))
+    V = rng.standard_normal((N, 1, d))
+    _, _, rp, ci, vals = oracle.compress(A, B, 0.5)
+    assert rp.tolist() == [0, 1]
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    for r in range(H_r):
+        assert np.abs(O[:, r, :] - W[r, 0] * (A[0] @ V[:, 0, :])).max() < 1e-12
+
+
+def test_gqa_groups_are_consecutive_heads():
+    rng = np.random.default_rng(2)
+    N, B, H_s, H_r, H_kv, d = 32, 16, 2, 6, 3, 2
+    A = _random_causal_map(rng, H_s, N)
+    _, _, rp, ci, vals = oracle.compress(A, B, 1.0)
+    W = np.ones((H_r, H_s))
+    V = np.zeros((N, H_kv, d))
+    V[:, 1, :] = 1.0                     # only KV head 1 is non-zero
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    nz = [r for r in range(H_r) if np.abs(O[:, r, :]).max() > 0]
+    assert nz == [2, 3]                  # G = 2: receiver heads 2, 3 read KV head 1
+
+
+# ---- hand-worked example ----------------------------------------------------
+
+def test_handworked_example():
+    with open(os.path.join(GOLDEN, "handworked_n4_b2.json")) as f:
+        g = json.load(f)
+    A = np.array(g["A"])
+    W = np.array(g["W"])
+    V = np.array(g["V"])
+    B = g["B"]
+    assert np.abs(oracle.block_mass(A, B) - np.array(g["mass"])).max() < 1e-12
+    for case in g["cases"]:
+        mass, kept, rp, ci, vals = oracle.compress(A, B, case["p"])
+        assert [k.tolist() for k in kept] == case["kept"]
+        assert rp.tolist() == case["row_ptr"] and ci.tolist() == case["col_idx"]
+        O = oracle.retrieve(rp, ci, vals, W, V, 4, B)
+        assert np.abs(O[:, 0, 0] - np.array(case["O"])).max() < 1e-12
+
+
+# ---- P8: the harness detects planted mistakes in the oracle's output -------
+
+def test_planted_mistakes_are_detected():
+    from tests._compare import check_output
+    rng = np.random.default_rng(8)
+    N, B, H_s, H_r, H_kv, d = 96, 16, 3, 4, 2, 8
+    A = _random_causal_map(rng, H_s, N).astype(np.float32)
+    W = rng.standard_normal((H_r, H_s))
+    V = rng.standard_normal((N, H_kv, d))
+    mass, kept, rp, ci, vals = oracle.compress(A, B, 0.9)
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    check_output(O.astype(np.float32), O, "f32")
+    # flip one kept value
+    v2 = vals.copy()
+    v2[len(v2) // 2, 1, 3, 5] += 0.25
+    with pytest.raises(AssertionError):
+        check_output(oracle.retrieve(rp, ci, v2, W, V, N, B), O, "f16")
+    # drop one kept block
+    I = oracle.n_blocks(N, B) - 1
+    k2 = [k.copy() for k in kept]
+    k2[I] = k2[I][1:]
+    rp2, ci2, vals2 = oracle.build_bsr(A, B, k2)
+    with pytest.raises(AssertionError):
+        check_output(oracle.retrieve(rp2, ci2, vals2, W, V, N, B), O, "bf16")
+    with pytest.raises(AssertionError):
+        selection_ok(mass[I, : I + 1], kept[I], k2[I], 0.9)
+    # permute col_idx within a row
+    ci3 = ci.copy()
+    a, b = rp[I], rp[I] + 1
+    ci3[a], ci3[b] = ci3[b], ci3[a]
+    with pytest.raises(AssertionError):
+        check_output(oracle.retrieve(rp, ci3, vals, W, V, N, B), O, "f16")
+    with pytest.raises(AssertionError):
+        check_bsr_structure(rp, ci3, oracle.n_blocks(N, B))
+    # a heavier block swapped for a lighter one is not a valid tie
+    m = np.array([0.5, 0.3, 0.2])
+    with pytest.raises(AssertionError):
+        selection_ok(m, [0, 1], [0, 2], 0.75)
