@@ -1,0 +1,162 @@
+// C boundary of libmapflow: argument validation, status codes and error text.
+// Every entry point checks its arguments on the host before touching the GPU.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "mf_internal.h"
+
+namespace mf {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MF_OK;
+  return fail(MF_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int row_vec_bytes(const void* base, int N, int B, int esize) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(base);
+  for (int v = 16; v > esize; v >>= 1) {
+    if ((a % v) == 0 && ((int64_t)N * esize) % v == 0 && ((int64_t)B * esize) % v == 0)
+      return v;
+  }
+  return esize;
+}
+
+bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int d, const void* vals,
+                        const void* V, int64_t ldV, const void* O, int64_t ldO);
+
+}  // namespace mf
+
+namespace {
+
+bool valid_dtype(int dt) { return dt == MF_F32 || dt == MF_F16 || dt == MF_BF16; }
+bool valid_block(int B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+
+std::string fmt(const char* f, long long a, long long b = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, f, a, b);
+  return buf;
+}
+
+// Shared checks of the map geometry; returns MF_OK or records the error.
+int check_geom(const char* fn, int dtype, int H_s, int N, int B) {
+  using mf::fail;
+  std::string f = std::string(fn) + ": ";
+  if (!valid_dtype(dtype)) return fail(MF_ERR_INVALID, f + fmt("unknown dtype code %lld", dtype));
+  if (N < 1) return fail(MF_ERR_INVALID, f + fmt("N must be >= 1 (got %lld)", N));
+  if (!valid_block(B)) return fail(MF_ERR_INVALID, f + fmt("B must be 16, 32, 64 or 128 (got %lld)", B));
+  if (H_s < 1 || H_s > 64) return fail(MF_ERR_INVALID, f + fmt("H_s must be in [1, 64] (got %lld)", H_s));
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_abi_version(void) { return MF_ABI_VERSION; }
+
+const char* mf_status_string(int status) {
+  switch (status) {
+    case MF_OK: return "MF_OK";
+    case MF_ERR_INVALID: return "MF_ERR_INVALID: invalid argument";
+    case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED: valid arguments, combination not built";
+    case MF_ERR_CAPACITY: return "MF_ERR_CAPACITY: BSR larger than the given capacity";
+    case MF_ERR_HIP: return "MF_ERR_HIP: HIP runtime error";
+    default: return "unknown mapflow status";
+  }
+}
+
+const char* mf_last_error(void) { return mf::g_last_error.c_str(); }
+
+int mf_block_mass(const void* A, int dtype, int H_s, int N, int B, float* mass,
+                  void* stream) {
+  int st = check_geom("mf_block_mass", dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (!A || !mass) return mf::fail(MF_ERR_INVALID, "mf_block_mass: null pointer");
+  return mf::hip_check(
+      mf::launch_block_mass(A, dtype, H_s, N, B, mass, (hipStream_t)stream),
+      "mf_block_mass launch");
+}
+
+size_t mf_topp_workspace_bytes(int N, int B) {
+  if (N < 1 || B < 1) return 0;
+  const size_t T = (size_t)mf::blocks_of(N, B);
+  const size_t bytes = (T * T + T) * sizeof(int32_t);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
+                       int N, int B, float p, int32_t* row_ptr,
+                       int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                       int64_t* nnzb_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  const char* fn = "mf_topp_select_bsr";
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (!mass || !A || !row_ptr || !workspace)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (cap_nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": cap_nnzb < 0");
+  if (cap_nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with cap_nnzb > 0");
+  if (!(p > 0.0f && p <= 1.0f))  // also rejects NaN
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": p must be in (0, 1]");
+  const int T = mf::blocks_of(N, B);
+  if (T > 4096)
+    return mf::fail(MF_ERR_UNSUPPORTED, std::string(fn) + fmt(": T = %lld block rows > 4096", T));
+  if (workspace_bytes < mf_topp_workspace_bytes(N, B))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          (long long)workspace_bytes,
+                                                          (long long)mf_topp_workspace_bytes(N, B)));
+  hipStream_t s = (hipStream_t)stream;
+  st = mf::hip_check(mf::launch_topp_bsr(mass, A, dtype, H_s, N, B, p, row_ptr,
+                                         col_idx, vals, cap_nnzb, workspace, s),
+                     "mf_topp_select_bsr launch");
+  if (st != MF_OK || !nnzb_out) return st;
+  int32_t nnzb = 0;
+  st = mf::hip_check(hipMemcpyAsync(&nnzb, row_ptr + T, sizeof nnzb,
+                                    hipMemcpyDeviceToHost, s),
+                     "mf_topp_select_bsr nnzb read-back");
+  if (st != MF_OK) return st;
+  st = mf::hip_check(hipStreamSynchronize(s), "mf_topp_select_bsr synchronise");
+  if (st != MF_OK) return st;
+  *nnzb_out = nnzb;
+  if (nnzb > cap_nnzb)
+    return mf::fail(MF_ERR_CAPACITY, std::string(fn) + fmt(": nnzb = %lld exceeds cap_nnzb = %lld",
+                                                           nnzb, cap_nnzb));
+  return MF_OK;
+}
+
+int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
+                      const void* vals, int64_t nnzb, int dtype, int H_s,
+                      int N, int B, const float* W, int H_r, const void* V,
+                      int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                      void* stream) {
+  const char* fn = "mf_retrieve_fused";
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (!row_ptr || !W || !V || !O) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": nnzb < 0");
+  if (nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with nnzb > 0");
+  if (H_r < 1 || H_r > 64) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": H_r must be in [1, 64] (got %lld)", H_r));
+  if (H_kv < 1 || H_r % H_kv != 0)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": H_r = %lld is not a multiple of H_kv = %lld", H_r, H_kv));
+  if (d != 64 && d != 128) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": d must be 64 or 128 (got %lld)", d));
+  if (ldV < (int64_t)H_kv * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldV < H_kv*d");
+  if (ldO < (int64_t)H_r * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldO < H_r*d");
+  return mf::launch_retrieve(row_ptr, col_idx, vals, nnzb, dtype, H_s, N, B, W,
+                             H_r, V, H_kv, d, ldV, O, ldO, (hipStream_t)stream);
+}
+
+}  // extern "C"

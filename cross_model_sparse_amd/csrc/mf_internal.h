@@ -1,0 +1,107 @@
+// Internal declarations shared by the libmapflow translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "mapflow.h"
+
+namespace mf {
+
+// Records a message for mf_last_error() and returns `st`.
+int fail(int st, const std::string& msg);
+// Checks a HIP status after a launch or runtime call.
+int hip_check(hipError_t e, const char* what);
+
+inline int blocks_of(int N, int B) { return (N + B - 1) / B; }
+inline int dtype_bytes(int dt) { return dt == MF_F32 ? 4 : 2; }
+
+// Largest load width in bytes (16, 8, 4 or the element size) such that every
+// row segment of a block tile starts on that alignment.
+int row_vec_bytes(const void* base, int N, int B, int esize);
+
+// Kernel launchers (one per translation unit); arguments already validated.
+hipError_t launch_block_mass(const void* A, int dt, int H_s, int N, int B,
+                             float* mass, hipStream_t st);
+hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
+                           int N, int B, float p, int32_t* row_ptr,
+                           int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                           void* workspace, hipStream_t st);
+int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
+                    const void* vals, int64_t nnzb, int dt, int H_s, int N,
+                    int B, const float* W, int H_r, const void* V, int H_kv,
+                    int d, int64_t ldV, void* O, int64_t ldO, hipStream_t st);
+
+}  // namespace mf
+
+// ---- device helpers -------------------------------------------------------
+
+namespace mfd {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float(((unsigned)h) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(unsigned short h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ unsigned short f32_to_f16(float f) {
+  return __builtin_bit_cast(unsigned short, (_Float16)f);
+}
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  return (unsigned)f32_to_f16(lo) | ((unsigned)f32_to_f16(hi) << 16);
+}
+// Two bf16 values packed in a dword -> two fp16 values (RNE).
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned v) {
+  return pack_f16x2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+
+// Storage-type tags: S is the element type in memory.
+struct TF32 {
+  using S = float;
+  static __device__ __forceinline__ float tof(S x) { return x; }
+  static __device__ __forceinline__ S fromf(float f) { return f; }
+};
+struct TF16 {
+  using S = unsigned short;
+  static __device__ __forceinline__ float tof(S x) { return f16_to_f32(x); }
+  static __device__ __forceinline__ S fromf(float f) { return f32_to_f16(f); }
+};
+struct TBF16 {
+  using S = unsigned short;
+  static __device__ __forceinline__ float tof(S x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ S fromf(float f) { return f32_to_bf16(f); }
+};
+
+// Vector of VEC bytes used for global loads and stores.
+template <int VEC> struct VecT;
+template <> struct VecT<16> { using T = uint4; };
+template <> struct VecT<8> { using T = uint2; };
+template <> struct VecT<4> { using T = unsigned; };
+template <> struct VecT<2> { using T = unsigned short; };
+
+// Sum, in fp32, of the elements packed in one vector.
+template <class TT, int VEC>
+__device__ __forceinline__ float vec_sum(const typename VecT<VEC>::T& v) {
+  constexpr int ES = sizeof(typename TT::S);
+  constexpr int NE = VEC / ES;
+  const typename TT::S* e = reinterpret_cast<const typename TT::S*>(&v);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NE; ++j) s += TT::tof(e[j]);
+  return s;
+}
+
+}  // namespace mfd

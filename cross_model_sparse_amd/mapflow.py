@@ -1,0 +1,208 @@
+"""Python binding of libmapflow (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers, sizes and the current HIP stream to the C boundary declared in
+include/mapflow.h, and turns a non-OK status into an exception.  No arithmetic
+of the method runs here: block mass, Top-p selection, BSR build and the fused
+retrieval all run in the library's HIP kernels.  If the library cannot be
+loaded the functions raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmapflow.so"
+
+MF_OK, MF_ERR_INVALID, MF_ERR_UNSUPPORTED, MF_ERR_CAPACITY, MF_ERR_HIP = range(5)
+MF_F32, MF_F16, MF_BF16 = 0, 1, 2
+
+_DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_BF16}
+
+EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
+            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_retrieve_fused")
+
+
+class MapflowError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class CapacityError(MapflowError):
+    def __init__(self, status: int, msg: str, nnzb: int):
+        super().__init__(status, msg)
+        self.nnzb = nnzb
+
+
+_lib = None
+
+
+def lib_path() -> Path:
+    return Path(os.environ.get("MAPFLOW_LIB", _LIB_PATH))
+
+
+def load() -> ctypes.CDLL:
+    """Loads libmapflow.so (built by cross_model_sparse_amd.build) once."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = lib_path()
+    if not p.exists():
+        raise RuntimeError(f"libmapflow not built: {p} is missing "
+                           "(run python -m cross_model_sparse_amd.build)")
+    L = ctypes.CDLL(str(p))
+    c_int, c_i64, c_sz, c_vp, c_f = (ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_float)
+    L.mf_abi_version.restype = c_int
+    L.mf_abi_version.argtypes = []
+    L.mf_status_string.restype = ctypes.c_char_p
+    L.mf_status_string.argtypes = [c_int]
+    L.mf_last_error.restype = ctypes.c_char_p
+    L.mf_last_error.argtypes = []
+    L.mf_block_mass.restype = c_int
+    L.mf_block_mass.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp]
+    L.mf_topp_workspace_bytes.restype = c_sz
+    L.mf_topp_workspace_bytes.argtypes = [c_int, c_int]
+    L.mf_topp_select_bsr.restype = c_int
+    L.mf_topp_select_bsr.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_f, c_vp,
+                                     c_vp, c_vp, c_i64, ctypes.POINTER(c_i64), c_vp,
+                                     c_sz, c_vp]
+    L.mf_retrieve_fused.restype = c_int
+    L.mf_retrieve_fused.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
+                                    c_vp, c_int, c_vp, c_int, c_int, c_i64, c_vp, c_i64,
+                                    c_vp]
+    _lib = L
+    return L
+
+
+def _check(st: int, nnzb: int | None = None) -> None:
+    if st == MF_OK:
+        return
+    L = load()
+    msg = L.mf_last_error().decode() or L.mf_status_string(st).decode()
+    if st == MF_ERR_CAPACITY:
+        raise CapacityError(st, msg, nnzb if nnzb is not None else -1)
+    raise MapflowError(st, msg)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dcode(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise MapflowError(MF_ERR_INVALID, f"unsupported dtype {t.dtype}") from None
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MapflowError(MF_ERR_INVALID, "tensors must be on the GPU")
+
+
+def abi_version() -> int:
+    return load().mf_abi_version()
+
+
+def topp_workspace_bytes(N: int, B: int) -> int:
+    return int(load().mf_topp_workspace_bytes(N, B))
+
+
+def block_mass(A: torch.Tensor, B: int, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """mass[T][T] fp32 of a contiguous [H_s][N][N] sender map (mf_block_mass)."""
+    _need_cuda(A)
+    H_s, N, N2 = A.shape
+    if N2 != N or not A.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "A must be a contiguous [H_s][N][N] tensor")
+    T = -(-N // B)
+    if out is None:
+        out = torch.empty(T, T, dtype=torch.float32, device=A.device)
+    _check(load().mf_block_mass(_ptr(A), _dcode(A), H_s, N, B, _ptr(out), _stream(stream)))
+    return out
+
+
+def topp_select_bsr(mass: torch.Tensor, A: torch.Tensor, B: int, p: float,
+                    cap_nnzb: int | None = None, row_ptr=None, col_idx=None, vals=None,
+                    workspace=None, sync: bool = True, stream=None):
+    """Top-p selection + BSR build (mf_topp_select_bsr).
+
+    Returns (row_ptr, col_idx, vals, nnzb).  With ``cap_nnzb`` None the call
+    first learns nnzb with capacity 0, then allocates exactly and runs again.
+    With ``sync=False`` nothing is read back and nnzb is returned as None."""
+    _need_cuda(mass, A)
+    H_s, N, _ = A.shape
+    T = -(-N // B)
+    L = load()
+    dev = A.device
+    if workspace is None:
+        workspace = torch.empty(topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    if cap_nnzb is None:
+        n = ctypes.c_int64(0)
+        st = L.mf_topp_select_bsr(_ptr(mass), _ptr(A), _dcode(A), H_s, N, B, float(p),
+                                  _ptr(row_ptr), None, None, 0, ctypes.byref(n),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+        if st not in (MF_OK, MF_ERR_CAPACITY):
+            _check(st)
+        cap_nnzb = int(n.value)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap_nnzb, 1), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((max(cap_nnzb, 1), H_s, B, B), dtype=A.dtype, device=dev)
+    n = ctypes.c_int64(-1)
+    st = L.mf_topp_select_bsr(_ptr(mass), _ptr(A), _dcode(A), H_s, N, B, float(p),
+                              _ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(cap_nnzb),
+                              ctypes.byref(n) if sync else None, _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    _check(st, int(n.value))
+    nnzb = int(n.value) if sync else None
+    return row_ptr, col_idx, vals, nnzb
+
+
+def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                   nnzb: int, W: torch.Tensor, V: torch.Tensor, N: int, B: int,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """O[N][H_r][d] = fused head-mapped BSR retrieval (mf_retrieve_fused).
+
+    V may be a [N][H_kv][d] tensor or a row-strided view whose last two dims
+    are contiguous (e.g. a slice of a fused QKV projection)."""
+    _need_cuda(row_ptr, col_idx, vals, W, V)
+    H_s = vals.shape[1]
+    H_r = W.shape[0]
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != H_s:
+        raise MapflowError(MF_ERR_INVALID, "W must be a contiguous fp32 [H_r][H_s] tensor")
+    if V.dim() != 3 or V.stride(2) != 1 or V.stride(1) != V.shape[2]:
+        raise MapflowError(MF_ERR_INVALID, "V must be [N][H_kv][d] with contiguous rows")
+    if V.dtype != vals.dtype:
+        raise MapflowError(MF_ERR_INVALID, "V and vals must share a dtype")
+    H_kv, d = V.shape[1], V.shape[2]
+    if out is None:
+        out = torch.empty(N, H_r, d, dtype=V.dtype, device=V.device)
+    if out.dim() != 3 or out.stride(2) != 1 or out.stride(1) != d:
+        raise MapflowError(MF_ERR_INVALID, "out must be [N][H_r][d] with contiguous rows")
+    _check(load().mf_retrieve_fused(_ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(nnzb),
+                                    _dcode(V), H_s, N, B, _ptr(W), H_r, _ptr(V), H_kv, d,
+                                    V.stride(0), _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def compress(A: torch.Tensor, B: int, p: float, cap_nnzb: int | None = None, stream=None):
+    """Block mass -> Top-p -> BSR on the GPU.  Returns (mass, row_ptr, col_idx, vals, nnzb)."""
+    mass = block_mass(A, B, stream=stream)
+    row_ptr, col_idx, vals, nnzb = topp_select_bsr(mass, A, B, p, cap_nnzb=cap_nnzb,
+                                                   stream=stream)
+    return mass, row_ptr, col_idx, vals, nnzb

@@ -1,0 +1,171 @@
+/*
+ * libmapflow -- MapFlow attention-map compression and fused head-mapped
+ * retrieval, native on AMD Instinct MI355X (gfx950).
+ *
+ * MapFlow ("Accelerating Cross-Model LLM Inference via Attention Map Reuse",
+ * montaan.com/papers/2610.14688; PKU-DAIR article aitest123.com/news/zaoi86)
+ * lets a receiver model reuse a sender model's attention maps.  The sender's
+ * causal maps are compressed by block-level Top-p into Block Sparse Row form
+ * (paper page, "Practical Implementation Details" and highlight 3; article,
+ * third section, first component: block statistics first, then the choice of
+ * blocks).  For each reuse receiver layer a fused kernel reads only the kept
+ * blocks, mixes the sender heads into each receiver head with the learned
+ * linear head map W, and multiplies by the receiver's own values, producing
+ * the attention output with no dense receiver map in memory (paper page,
+ * "MapFlow System Design" item 3 and highlight 4; article, third component).
+ *
+ * Notation: N tokens, block size B, T = ceil(N/B); H_s sender heads; H_r
+ * receiver heads; H_kv receiver KV heads, G = H_r / H_kv, receiver head r
+ * reads KV head r / G; d head dimension.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked "device" are device memory owned by the caller; the
+ *    library never allocates, frees or retains them.  Pointers marked "host"
+ *    are host memory.
+ *  - Every call validates its arguments on the host before any GPU work and
+ *    returns a status; it never aborts or throws across the boundary.  On a
+ *    non-OK status mf_last_error() holds a message (thread-local).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Buffers must stay alive until the stream has finished.
+ *    The only host synchronisation is the one documented at
+ *    mf_topp_select_bsr.
+ *  - Dtype codes: MF_F32 = 0, MF_F16 = 1, MF_BF16 = 2.
+ *  - The library holds no global state besides the thread-local error text
+ *    and is safe to call from several host threads on different streams.
+ */
+#ifndef MAPFLOW_H
+#define MAPFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MF_ABI_VERSION 1
+
+typedef enum {
+  MF_OK = 0,
+  MF_ERR_INVALID = 1,     /* bad argument (null pointer, size, dtype, p, stride) */
+  MF_ERR_UNSUPPORTED = 2, /* valid arguments, combination not built */
+  MF_ERR_CAPACITY = 3,    /* BSR output larger than the caller's capacity */
+  MF_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} mf_status;
+
+typedef enum { MF_F32 = 0, MF_F16 = 1, MF_BF16 = 2 } mf_dtype;
+
+/* Returns MF_ABI_VERSION of the built library. */
+int mf_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* mf_status_string(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* mf_last_error(void);
+
+/*
+ * Block mass -- the compressor's block statistic (article, third section,
+ * first component; paper page, highlight 3).
+ *
+ *   mass[I][J] = (1/H_s) * sum_h sum_{i in block I, i<N} sum_{j in block J, j<N} A[h][i][j]
+ *
+ * for the causal blocks J <= I; entries with J > I are written as 0.
+ *
+ *  A     device, [H_s][N][N] row-major, dtype `dtype`: the sender layer's
+ *        causal attention maps (rows sum to 1; entries above the diagonal are
+ *        expected to be 0 but are read and summed as given inside the
+ *        diagonal blocks).  Only the causal block tiles are read.
+ *  mass  device, [T][T] float32, written completely.
+ *  The per-block sum is formed with fp32 partial sums of at most 8
+ *  consecutive elements combined in fp64, then rounded once to fp32.
+ *  Errors: MF_ERR_INVALID for a null pointer, N < 1, B not in
+ *  {16,32,64,128}, H_s not in [1,64] or an unknown dtype.
+ */
+int mf_block_mass(const void* A, int dtype, int H_s, int N, int B,
+                  float* mass, void* stream);
+
+/* Workspace bytes mf_topp_select_bsr needs for (N, B). */
+size_t mf_topp_workspace_bytes(int N, int B);
+
+/*
+ * Block-level Top-p selection and BSR build (paper page, highlight 3 and
+ * "Practical Implementation Details"; article, third section, first and
+ * second components).
+ *
+ * For each block row I, the candidates J = 0..I are ordered by decreasing
+ * mass[I][J] (equal fp32 masses: lower J first) and kept until the running
+ * sum, accumulated in fp64 in that order, first reaches p * total, where
+ * total is the fp64 sum of mass[I][0..I] in column order; the block that
+ * reaches it is kept.  p == 1 keeps every causal block.  The kept columns of
+ * each row are stored in ascending order.
+ *
+ *  mass      device, [T][T] float32 from mf_block_mass.
+ *  A         device, the same [H_s][N][N] map (source of the kept tiles).
+ *  p         Top-p threshold, 0 < p <= 1.
+ *  row_ptr   device, [T+1] int32, written: row_ptr[0] = 0,
+ *            row_ptr[I+1] - row_ptr[I] = blocks kept in row I, row_ptr[T] = nnzb.
+ *  col_idx   device, [cap_nnzb] int32, written for k < nnzb.
+ *  vals      device, [cap_nnzb][H_s][B][B] of `dtype`, written for k < nnzb:
+ *            vals[k][h][i][c] = A[h][I*B+i][J*B+c] copied bit for bit, 0 where
+ *            I*B+i >= N or J*B+c >= N.
+ *  cap_nnzb  capacity of col_idx/vals in blocks (>= 0).
+ *  nnzb_out  host, may be NULL.  If non-NULL the call synchronises `stream`
+ *            after enqueueing its work, stores nnzb there, and returns
+ *            MF_ERR_CAPACITY if nnzb > cap_nnzb.  If NULL the call does not
+ *            synchronise; read row_ptr[T] to learn nnzb.
+ *  workspace device, >= mf_topp_workspace_bytes(N, B) bytes of scratch.
+ *  When nnzb > cap_nnzb the kernels leave col_idx and vals untouched; row_ptr
+ *  is always valid, so the caller can reallocate and call again.
+ *  Errors: MF_ERR_INVALID for null pointers, bad N/B/H_s/dtype, p NaN or
+ *  outside (0, 1], cap_nnzb < 0 or a workspace that is too small;
+ *  MF_ERR_UNSUPPORTED if T > 4096; MF_ERR_CAPACITY as above.
+ */
+int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
+                       int N, int B, float p, int32_t* row_ptr,
+                       int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                       int64_t* nnzb_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Fused head-mapped BSR retrieval (paper page, "MapFlow System Design" item 3,
+ * highlights 2 and 4; article, second section and third component).
+ *
+ * For every kept block k = (I, J) and receiver head r:
+ *   Ahat_k[r] = sum_s W[r][s] * vals[k][s]                       (B x B, on chip)
+ *   O[I*B+i][r][:] += sum_c Ahat_k[r][i][c] * V[J*B+c][r/G][:]
+ * accumulated in fp32 over the row's kept blocks; O is written once, rounded
+ * to `dtype` with round-to-nearest-even.  Ahat is never written to memory.
+ * Rows with no kept block get O = 0.
+ *
+ *  row_ptr, col_idx, vals  device, the BSR state from mf_topp_select_bsr
+ *            (or any BSR of the same layout: row_ptr monotone from 0, col_idx
+ *            in [0, T)); `nnzb` is the number of blocks in vals.  Blocks with
+ *            a column outside [0, T) and indices k outside [0, nnzb) are
+ *            skipped rather than read.
+ *  W         device, [H_r][H_s] float32, row-major.
+ *  V         device, rows of H_kv*d elements of `dtype` at stride ldV
+ *            elements (ldV >= H_kv*d, so V may be a slice of a fused QKV
+ *            tensor): V[n][g][e] at V[n*ldV + g*d + e], n < N.
+ *  O         device, O[n][r][e] at O[n*ldO + r*d + e], ldO >= H_r*d.
+ *  Precision: for MF_F16 and MF_BF16 the contractions run on fp16 matrix
+ *  cores with fp32 accumulation; bf16 inputs are converted to fp16 on chip
+ *  (exact for |x| in [2^-17, 65504]), W and the mixed map are rounded to
+ *  fp16.  V entries must lie within +-65504 and sum_s |W[r][s]| must stay
+ *  below 65504 for this to be meaningful.  MF_F32 runs in fp32 throughout.
+ *  Errors: MF_ERR_INVALID for null pointers, N < 1, nnzb < 0, bad B, d not
+ *  in {64,128}, H_s/H_r not in [1,64], H_kv < 1, H_r % H_kv != 0, ldV or ldO
+ *  too small, unknown dtype.
+ */
+int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
+                      const void* vals, int64_t nnzb, int dtype, int H_s,
+                      int N, int B, const float* W, int H_r, const void* V,
+                      int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAPFLOW_H */

@@ -1,0 +1,158 @@
+"""C boundary checks that need no GPU: the library loads, exports every symbol
+declared in include/mapflow.h, and rejects bad arguments on the host before any
+GPU work (every call below returns before its first HIP call)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import cross_model_sparse_amd as mf
+from cross_model_sparse_amd import mapflow as mfb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mapflow.h")
+
+FAKE = 0x10000   # never dereferenced: validation fails before any use
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mf_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mf.load()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(mf.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", str(mf.lib_path())],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mf_[a-z_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings(L):
+    assert mf.abi_version() == 1
+    for st in range(5):
+        assert L.mf_status_string(st)
+    assert b"unknown" in L.mf_status_string(99)
+
+
+def test_workspace_size(L):
+    assert mf.topp_workspace_bytes(8192, 64) >= (128 * 128 + 128) * 4
+    assert mf.topp_workspace_bytes(8192, 64) % 256 == 0
+    assert mf.topp_workspace_bytes(0, 64) == 0
+
+
+def _last(L):
+    return L.mf_last_error().decode()
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((None, 2, 40, 8192, 64), "null"),
+    ((FAKE, 7, 40, 8192, 64), "dtype"),
+    ((FAKE, 2, 0, 8192, 64), "H_s"),
+    ((FAKE, 2, 65, 8192, 64), "H_s"),
+    ((FAKE, 2, 40, 0, 64), "N must"),
+    ((FAKE, 2, 40, 8192, 48), "B must"),
+])
+def test_block_mass_rejects(L, args, frag):
+    A, dt, H_s, N, B = args
+    st = L.mf_block_mass(A, dt, H_s, N, B, FAKE if A else FAKE, None)
+    assert st == mf.MF_ERR_INVALID
+    assert frag in _last(L)
+
+
+def _topp(L, **kw):
+    a = dict(mass=FAKE, A=FAKE, dt=2, H_s=40, N=8192, B=64, p=0.9, row_ptr=FAKE,
+             col_idx=FAKE, vals=FAKE, cap=10, nnzb_out=None, ws=FAKE,
+             ws_bytes=mf.topp_workspace_bytes(8192, 64))
+    a.update(kw)
+    return L.mf_topp_select_bsr(a["mass"], a["A"], a["dt"], a["H_s"], a["N"], a["B"],
+                                a["p"], a["row_ptr"], a["col_idx"], a["vals"], a["cap"],
+                                a["nnzb_out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,st,frag", [
+    (dict(p=0.0), mf.MF_ERR_INVALID, "p must"),
+    (dict(p=1.5), mf.MF_ERR_INVALID, "p must"),
+    (dict(p=float("nan")), mf.MF_ERR_INVALID, "p must"),
+    (dict(p=-0.1), mf.MF_ERR_INVALID, "p must"),
+    (dict(mass=None), mf.MF_ERR_INVALID, "null"),
+    (dict(ws=None), mf.MF_ERR_INVALID, "null"),
+    (dict(cap=-1), mf.MF_ERR_INVALID, "cap_nnzb"),
+    (dict(vals=None), mf.MF_ERR_INVALID, "null col_idx/vals"),
+    (dict(ws_bytes=100), mf.MF_ERR_INVALID, "workspace"),
+    (dict(N=4096 * 128 + 1, B=128), mf.MF_ERR_UNSUPPORTED, "4096"),
+    (dict(B=8), mf.MF_ERR_INVALID, "B must"),
+])
+def test_topp_rejects(L, kw, st, frag):
+    assert _topp(L, **kw) == st
+    assert frag in _last(L)
+
+
+def _retr(L, **kw):
+    a = dict(row_ptr=FAKE, col_idx=FAKE, vals=FAKE, nnzb=5, dt=2, H_s=40, N=8192,
+             B=64, W=FAKE, H_r=32, V=FAKE, H_kv=8, d=128, ldV=8 * 128, O=FAKE,
+             ldO=32 * 128)
+    a.update(kw)
+    return L.mf_retrieve_fused(a["row_ptr"], a["col_idx"], a["vals"], a["nnzb"], a["dt"],
+                               a["H_s"], a["N"], a["B"], a["W"], a["H_r"], a["V"],
+                               a["H_kv"], a["d"], a["ldV"], a["O"], a["ldO"], None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(H_r=30), "multiple of H_kv"),
+    (dict(H_kv=0), "multiple of H_kv"),
+    (dict(H_r=65, H_kv=5), "H_r must"),
+    (dict(d=96), "d must"),
+    (dict(ldV=8 * 128 - 1), "ldV"),
+    (dict(ldO=100), "ldO"),
+    (dict(W=None), "null"),
+    (dict(nnzb=-1), "nnzb"),
+    (dict(vals=None), "null col_idx/vals"),
+    (dict(dt=3), "dtype"),
+])
+def test_retrieve_rejects(L, kw, frag):
+    assert _retr(L, **kw) == mf.MF_ERR_INVALID
+    assert frag in _last(L)
+
+
+def test_last_error_is_thread_local(L):
+    import threading
+    _retr(L, d=96)
+    seen = {}
+
+    def other():
+        seen["msg"] = L.mf_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "d must" in _last(L)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(mf.MapflowError):
+        mf.block_mass(torch.zeros(2, 8, 8), 16)
+
+
+def test_header_documents_every_entry_point():
+    src = open(HEADER).read()
+    for name in declared_functions():
+        m = re.search(r"\n(?:int|size_t|const char\*)\s+" + name + r"\(", src)
+        assert m, name
+        before = src[max(0, m.start() - 1500):m.start()]
+        assert before.rstrip().endswith("*/"), f"{name} has no comment block"
