@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the MapFlow retrieval hot path on one MI355X.
+
+Workload: the 14B->8B-like pair, 24 reuse layers back to back (N = 8192,
+B = 64, H_s = 40, H_r = 32, H_kv = 8, d = 128, bf16, p = 0.9), seeded
+synthetic structured sender maps, one distinct sender map per layer.
+
+One step = the whole hot path over all 24 layers, inputs resident in HBM:
+    block mass -> Top-p selection + BSR build -> fused head-mapped retrieval
+with no host synchronisation inside the step (BSR capacities are sized in the
+untimed warm-up).  `value` is the metric: fused-retrieval query-tokens/s per
+layer = 24 * N * steps / (sum of retrieval kernel times), timed with HIP
+events on the launch stream.  The line also carries the roofline of the
+retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
+bounded sample of block rows of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="reuse layers per step (default: the workload's 24)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU work for the oracle leg")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the retrieval path is built and measured "
+              "on a single MI355X (multi-GPU sharding by block rows is design-only). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cross_model_sparse_amd as mf
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mf.load()
+    dev = torch.device("cuda:0")
+    w = synth.workload("pair14b8b-bf16")
+    L = args.layers or w.layers
+    N, B, T = w.N, w.B, w.T
+    e = synth.DTYPE_BYTES[w.dtype]
+
+    # ---- inputs (untimed) ---------------------------------------------------
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        g = synth.gen_layer(w, layer=l, device=dev)
+        layers.append({"A": g["A"], "W": g["W"].to(dev), "V": g["V"].to(dev),
+                       "seed": g["seed"]})
+        log(f"generated layer {l} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+
+    # ---- capacities from one synchronous pass (untimed) ----------------------
+    for x in layers:
+        mass = mf.block_mass(x["A"], B)
+        rp, ci, vals, nnzb = mf.topp_select_bsr(mass, x["A"], B, w.p)
+        x.update(mass=mass, rp=rp, ci=ci, vals=vals, nnzb=nnzb,
+                 ws=torch.empty(mf.topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev),
+                 O=torch.empty(N, w.H_r, w.d, dtype=synth.torch_dtype(w.dtype), device=dev))
+    nnzbs = [x["nnzb"] for x in layers]
+    log(f"nnzb per layer: min {min(nnzbs)} max {max(nnzbs)} "
+        f"density {np.mean(nnzbs) / (T * (T + 1) / 2):.4f}")
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(record):
+        for x in layers:
+            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+            if record: e0.record(stream)
+            mf.block_mass(x["A"], B, out=x["mass"])
+            if record: e1.record(stream)
+            mf.topp_select_bsr(x["mass"], x["A"], B, w.p, cap_nnzb=x["nnzb"],
+                               row_ptr=x["rp"], col_idx=x["ci"], vals=x["vals"],
+                               workspace=x["ws"], sync=False)
+            if record: e2.record(stream)
+            mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
+                              N, B, out=x["O"])
+            if record:
+                e3.record(stream)
+                rec.append((e0, e1, e2, e3))
+
+    rec = []
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+
+    t_mass = sum(a.elapsed_time(b) for a, b, c, d in rec) / 1e3
+    t_topp = sum(b.elapsed_time(c) for a, b, c, d in rec) / 1e3
+    t_retr = sum(c.elapsed_time(d) for a, b, c, d in rec) / 1e3
+    K = args.steps
+    n_retr = K * L
+    ms_per_step = wall / K * 1e3
+
+    # algorithmic bytes / flops of one retrieval launch, summed over layers
+    def retr_bytes(nz):
+        return (nz * w.H_s * B * B * e + N * w.H_kv * w.d * e + N * w.H_r * w.d * e
+                + 4 * (T + 1 + nz) + 4 * w.H_r * w.H_s)
+
+    def retr_flops(nz):
+        return 2.0 * nz * w.H_r * B * B * (w.H_s + w.d)
+
+    bytes_step = sum(retr_bytes(nz) for nz in nnzbs)
+    flops_step = sum(retr_flops(nz) for nz in nnzbs)
+    achieved_gbs = bytes_step * K / t_retr / 1e9
+    achieved_tflops = flops_step * K / t_retr / 1e12
+    causal_bytes = sum(w.H_s * B * B * e * (T * (T + 1) // 2) for _ in nnzbs)  # K1 tiles read
+    gather_bytes = sum(2 * nz * w.H_s * B * B * e for nz in nnzbs)
+
+    out = {
+        "metric": "fused retrieval query-tokens/s per layer + % of HBM/MFMA roofline at N=8192",
+        "value": N * n_retr / t_retr,
+        "unit": "query-tokens/s per layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "pair14b8b-bf16: 14B->8B-like pair, 24 reuse layers",
+                   "N": N, "B": B, "H_s": w.H_s, "H_r": w.H_r, "H_kv": w.H_kv,
+                   "d": w.d, "p": w.p, "layers": L, "storage_dtype": "bf16",
+                   "compute": "fp16 MFMA, fp32 accumulate",
+                   "maps": "structured: sink + band 512 + 4 stripes/head + N(0,1) noise"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_retrieve_mfma",
+                     "bytes_per_launch": bytes_step / L,
+                     "mfma_tflops": achieved_tflops,
+                     "mfma_frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS},
+        "kernels_ms_per_layer": {"block_mass": t_mass / n_retr * 1e3,
+                                 "topp_select_bsr": t_topp / n_retr * 1e3,
+                                 "retrieve_fused": t_retr / n_retr * 1e3},
+        "roofline_kernels": {
+            "block_mass_GBs": causal_bytes * K / t_mass / 1e9,
+            "topp_select_bsr_GBs": gather_bytes * K / t_topp / 1e9},
+        "e2e_query_tokens_per_s_per_layer": N * n_retr / wall,
+        "nnzb_per_layer": {"min": min(nnzbs), "max": max(nnzbs),
+                           "mean": float(np.mean(nnzbs))},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_leg(w, layers[0], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_leg(w, layer, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of block rows of
+    layer 0 (the same device tensors, copied to the host row by row)."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        blas_threads = os.cpu_count()
+    A = layer["A"]
+    W = layer["W"].cpu().numpy()
+    V = layer["V"].float().cpu().numpy()
+    N, B, T = w.N, w.B, w.T
+
+    class RowSlab:
+        shape = tuple(A.shape)
+
+        def __getitem__(self, idx):
+            return A[idx].float().cpu().numpy()
+
+    view = RowSlab()
+    order = [T - 1 - 7 * i for i in range(T // 7)]   # every 7th block row, last first
+    t_comp = t_retr = 0.0
+    rows = 0
+    blocks = 0
+    for I in order:
+        c0 = time.perf_counter()
+        m = oracle.block_mass_row(view, B, I)
+        kept = oracle.topp_row(oracle.decision_masses(m), w.p)
+        tiles = [oracle.bsr_tile(view, B, I, int(J)) for J in kept]
+        c1 = time.perf_counter()
+        oracle.retrieve_row(I, kept, tiles, W, V, N, B)
+        c2 = time.perf_counter()
+        t_comp += c1 - c0
+        t_retr += c2 - c1
+        rows += 1
+        blocks += len(kept)
+        if t_comp + t_retr > budget_s:
+            break
+    tokens = rows * B
+    return {"value": tokens / t_retr, "unit": "query-tokens/s per layer",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"{rows} of {T} block rows of layer 0 (every 7th from the last; "
+                       f"{blocks} kept blocks); retrieval {t_retr:.2f}s, compression "
+                       f"(host copy + block mass + Top-p + tile gather) {t_comp:.2f}s; "
+                       f"host cpu_count {os.cpu_count()}")}
+
+
+if __name__ == "__main__":
+    main()
