@@ -86,6 +86,9 @@ def main():
         x.update(mass=mass, rp=rp, ci=ci, vals=vals, nnzb=nnzb,
                  ws=torch.empty(mf.topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev),
                  O=torch.empty(N, w.H_r, w.d, dtype=synth.torch_dtype(w.dtype), device=dev))
+    ws_r = torch.empty(max(1, mf.retrieve_workspace_bytes(N, B, w.H_kv, w.d,
+                                                          synth.torch_dtype(w.dtype))),
+                       dtype=torch.uint8, device=dev)
     nnzbs = [x["nnzb"] for x in layers]
     log(f"nnzb per layer: min {min(nnzbs)} max {max(nnzbs)} "
         f"density {np.mean(nnzbs) / (T * (T + 1) / 2):.4f}")
@@ -104,7 +107,7 @@ def main():
                                workspace=x["ws"], sync=False)
             if record: e2.record(stream)
             mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
-                              N, B, out=x["O"])
+                              N, B, out=x["O"], workspace=ws_r)
             if record:
                 e3.record(stream)
                 rec.append((e0, e1, e2, e3))

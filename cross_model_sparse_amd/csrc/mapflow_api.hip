@@ -33,9 +33,6 @@ int row_vec_bytes(const void* base, int N, int B, int esize) {
   return esize;
 }
 
-bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int d, const void* vals,
-                        const void* V, int64_t ldV, const void* O, int64_t ldO);
-
 }  // namespace mf
 
 namespace {
@@ -137,11 +134,16 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
   return MF_OK;
 }
 
+size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype) {
+  if (N < 1 || !valid_block(B) || H_kv < 1 || !valid_dtype(dtype)) return 0;
+  return mf::retrieve_workspace_bytes(N, B, H_kv, d, dtype);
+}
+
 int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                       const void* vals, int64_t nnzb, int dtype, int H_s,
                       int N, int B, const float* W, int H_r, const void* V,
                       int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "mf_retrieve_fused";
   int st = check_geom(fn, dtype, H_s, N, B);
   if (st != MF_OK) return st;
@@ -155,8 +157,14 @@ int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
   if (d != 64 && d != 128) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": d must be 64 or 128 (got %lld)", d));
   if (ldV < (int64_t)H_kv * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldV < H_kv*d");
   if (ldO < (int64_t)H_r * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldO < H_r*d");
+  const size_t need = mf::retrieve_workspace_bytes(N, B, H_kv, d, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          workspace ? (long long)workspace_bytes : 0LL,
+                                                          (long long)need));
   return mf::launch_retrieve(row_ptr, col_idx, vals, nnzb, dtype, H_s, N, B, W,
-                             H_r, V, H_kv, d, ldV, O, ldO, (hipStream_t)stream);
+                             H_r, V, H_kv, d, ldV, O, ldO, workspace, workspace_bytes,
+                             (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -31,7 +31,9 @@ hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
 int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     const void* vals, int64_t nnzb, int dt, int H_s, int N,
                     int B, const float* W, int H_r, const void* V, int H_kv,
-                    int d, int64_t ldV, void* O, int64_t ldO, hipStream_t st);
+                    int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
+                    size_t workspace_bytes, hipStream_t st);
+size_t retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dt);
 
 }  // namespace mf
 

@@ -23,7 +23,8 @@ MF_F32, MF_F16, MF_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_BF16}
 
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
-            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_retrieve_fused")
+            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_retrieve_workspace_bytes",
+            "mf_retrieve_fused")
 
 
 class MapflowError(RuntimeError):
@@ -71,10 +72,12 @@ def load() -> ctypes.CDLL:
     L.mf_topp_select_bsr.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_f, c_vp,
                                      c_vp, c_vp, c_i64, ctypes.POINTER(c_i64), c_vp,
                                      c_sz, c_vp]
+    L.mf_retrieve_workspace_bytes.restype = c_sz
+    L.mf_retrieve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     L.mf_retrieve_fused.restype = c_int
     L.mf_retrieve_fused.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
                                     c_vp, c_int, c_vp, c_int, c_int, c_i64, c_vp, c_i64,
-                                    c_vp]
+                                    c_vp, c_sz, c_vp]
     _lib = L
     return L
 
@@ -118,6 +121,10 @@ def abi_version() -> int:
 
 def topp_workspace_bytes(N: int, B: int) -> int:
     return int(load().mf_topp_workspace_bytes(N, B))
+
+
+def retrieve_workspace_bytes(N: int, B: int, H_kv: int, d: int, dtype: torch.dtype) -> int:
+    return int(load().mf_retrieve_workspace_bytes(N, B, H_kv, d, _DTYPE_CODE[dtype]))
 
 
 def block_mass(A: torch.Tensor, B: int, out: torch.Tensor | None = None,
@@ -175,7 +182,8 @@ def topp_select_bsr(mass: torch.Tensor, A: torch.Tensor, B: int, p: float,
 
 def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
                    nnzb: int, W: torch.Tensor, V: torch.Tensor, N: int, B: int,
-                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
     """O[N][H_r][d] = fused head-mapped BSR retrieval (mf_retrieve_fused).
 
     V may be a [N][H_kv][d] tensor or a row-strided view whose last two dims
@@ -194,9 +202,14 @@ def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Ten
         out = torch.empty(N, H_r, d, dtype=V.dtype, device=V.device)
     if out.dim() != 3 or out.stride(2) != 1 or out.stride(1) != d:
         raise MapflowError(MF_ERR_INVALID, "out must be [N][H_r][d] with contiguous rows")
+    need = retrieve_workspace_bytes(N, B, H_kv, d, V.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=V.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().mf_retrieve_fused(_ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(nnzb),
                                     _dcode(V), H_s, N, B, _ptr(W), H_r, _ptr(V), H_kv, d,
-                                    V.stride(0), _ptr(out), out.stride(0), _stream(stream)))
+                                    V.stride(0), _ptr(out), out.stride(0), _ptr(workspace),
+                                    ws_bytes, _stream(stream)))
     return out
 
 

@@ -128,6 +128,12 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
                        int64_t* nnzb_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Workspace bytes mf_retrieve_fused needs for (N, B, H_kv, d, dtype); 0 when
+ * the call needs none (fp32, d = 64 or B = 16).  It holds an fp16 copy of V
+ * laid out for the matrix cores (H_kv * ceil(N/B)*B * d * 2 bytes) plus one
+ * power-of-two range scale per 32-key chunk and KV head. */
+size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
+
 /*
  * Fused head-mapped BSR retrieval (paper page, "MapFlow System Design" item 3,
  * highlights 2 and 4; article, second section and third component).
@@ -149,20 +155,23 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
  *            elements (ldV >= H_kv*d, so V may be a slice of a fused QKV
  *            tensor): V[n][g][e] at V[n*ldV + g*d + e], n < N.
  *  O         device, O[n][r][e] at O[n*ldO + r*d + e], ldO >= H_r*d.
- *  Precision: for MF_F16 and MF_BF16 the contractions run on fp16 matrix
- *  cores with fp32 accumulation; bf16 inputs are converted to fp16 on chip
- *  (exact for |x| in [2^-17, 65504]), W and the mixed map are rounded to
- *  fp16.  V entries must lie within +-65504 and sum_s |W[r][s]| must stay
- *  below 65504 for this to be meaningful.  MF_F32 runs in fp32 throughout.
+ *  workspace device scratch of >= mf_retrieve_workspace_bytes(...) bytes
+ *            (may be NULL when that is 0); overwritten by the call.
+ *  Precision: for MF_F16 and MF_BF16 the head mix runs on fp16 (bf16 for bf16
+ *  maps, with W split into two bf16 halves so W enters exactly) matrix cores
+ *  with fp32 accumulation; the mixed map is rounded to fp16 and multiplied
+ *  with an fp16 copy of V (exact for bf16 values in [2^-17, 2^15]; larger
+ *  values are scaled by a power of two per 32-key chunk).  MF_F32 runs in
+ *  fp32 throughout.
  *  Errors: MF_ERR_INVALID for null pointers, N < 1, nnzb < 0, bad B, d not
  *  in {64,128}, H_s/H_r not in [1,64], H_kv < 1, H_r % H_kv != 0, ldV or ldO
- *  too small, unknown dtype.
+ *  too small, a missing or short workspace, unknown dtype.
  */
 int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                       const void* vals, int64_t nnzb, int dtype, int H_s,
                       int N, int B, const float* W, int H_r, const void* V,
                       int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,13 @@ def test_version_and_status_strings(L):
     assert b"unknown" in L.mf_status_string(99)
 
 
+def test_retrieve_workspace_size(L):
+    n = mf.retrieve_workspace_bytes(8192, 64, 8, 128, __import__("torch").bfloat16)
+    assert n >= 8 * 8192 * 128 * 2 and n % 256 == 0
+    assert mf.retrieve_workspace_bytes(256, 16, 4, 64, __import__("torch").float32) == 0
+    assert L.mf_retrieve_workspace_bytes(0, 64, 8, 128, 2) == 0
+
+
 def test_workspace_size(L):
     assert mf.topp_workspace_bytes(8192, 64) >= (128 * 128 + 128) * 4
     assert mf.topp_workspace_bytes(8192, 64) % 256 == 0
@@ -104,11 +111,12 @@ def test_topp_rejects(L, kw, st, frag):
 def _retr(L, **kw):
     a = dict(row_ptr=FAKE, col_idx=FAKE, vals=FAKE, nnzb=5, dt=2, H_s=40, N=8192,
              B=64, W=FAKE, H_r=32, V=FAKE, H_kv=8, d=128, ldV=8 * 128, O=FAKE,
-             ldO=32 * 128)
+             ldO=32 * 128, ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     return L.mf_retrieve_fused(a["row_ptr"], a["col_idx"], a["vals"], a["nnzb"], a["dt"],
                                a["H_s"], a["N"], a["B"], a["W"], a["H_r"], a["V"],
-                               a["H_kv"], a["d"], a["ldV"], a["O"], a["ldO"], None)
+                               a["H_kv"], a["d"], a["ldV"], a["O"], a["ldO"], a["ws"],
+                               a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,frag", [
@@ -122,6 +130,8 @@ def _retr(L, **kw):
     (dict(nnzb=-1), "nnzb"),
     (dict(vals=None), "null col_idx/vals"),
     (dict(dt=3), "dtype"),
+    (dict(ws=None), "workspace"),
+    (dict(ws_bytes=1000), "workspace"),
 ])
 def test_retrieve_rejects(L, kw, frag):
     assert _retr(L, **kw) == mf.MF_ERR_INVALID
