@@ -130,8 +130,10 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
 
 /* Workspace bytes mf_retrieve_fused needs for (N, B, H_kv, d, dtype); 0 when
  * the call needs none (fp32, d = 64 or B = 16).  It holds an fp16 copy of V
- * laid out for the matrix cores (H_kv * ceil(N/B)*B * d * 2 bytes) plus one
- * power-of-two range scale per 32-key chunk and KV head. */
+ * laid out for the matrix cores (H_kv * K * d * 2 bytes, K = ceil(N/B)*B
+ * rounded up to a multiple of 64 keys, zero past N) plus one 4-byte
+ * power-of-two range scale per 16-key chunk and KV head, each part aligned
+ * to 256 bytes. */
 size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
 
 /*
@@ -161,7 +163,7 @@ size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
  *  maps, with W split into two bf16 halves so W enters exactly) matrix cores
  *  with fp32 accumulation; the mixed map is rounded to fp16 and multiplied
  *  with an fp16 copy of V (exact for bf16 values in [2^-17, 2^15]; larger
- *  values are scaled by a power of two per 32-key chunk).  MF_F32 runs in
+ *  values are scaled by a power of two per 16-key chunk).  MF_F32 runs in
  *  fp32 throughout.
  *  Errors: MF_ERR_INVALID for null pointers, N < 1, nnzb < 0, bad B, d not
  *  in {64,128}, H_s/H_r not in [1,64], H_kv < 1, H_r % H_kv != 0, ldV or ldO
