@@ -160,7 +160,7 @@ def main():
         "config": {"workload": "pair14b8b-bf16: 14B->8B-like pair, 24 reuse layers",
                    "N": N, "B": B, "H_s": w.H_s, "H_r": w.H_r, "H_kv": w.H_kv,
                    "d": w.d, "p": w.p, "layers": L, "storage_dtype": "bf16",
-                   "compute": "fp16 MFMA, fp32 accumulate",
+                   "compute": "bf16 MFMA (W and mixed map as hi+lo bf16), fp32 accumulate",
                    "maps": "structured: sink + band 512 + 4 stripes/head + N(0,1) noise"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,

@@ -10,54 +10,43 @@
 //     Ahat_k[r] = sum_s W[r][s] * vals[k][s]
 //     O[I*B+i][r][:] += sum_c Ahat_k[r][i][c] * V[J*B+c][r/G][:]
 //
-// Kernels:
-//
-// k_prep_values   once per call: V (fp16/bf16, rows of stride ldV) becomes an
-//                 fp16 copy in the matrix-core operand layout
-//                 Vp[g][key/8][d][8] (eight consecutive keys of one head-dim
-//                 column are 16 contiguous bytes).  Each 16-key chunk of each
-//                 KV head gets a power-of-two scale 2^-e (e >= 0; e = 0 unless
-//                 |V| reaches 2^15) that keeps the copy in fp16 range; the
-//                 matching 2^e is folded into the mixed map before it is
-//                 rounded to fp16.
-//
-// k_retrieve_mfma (fp16/bf16, d = 128, B in {32,64,128}, H_r = 4*{2,4,6,8},
-//                  H_s <= 48, H_kv <= 8)
-//   Work item = (block row I, 16-row slice); one 256-thread workgroup owns all
-//   receiver heads and all of d for its 16 query rows, so every kept tile
-//   element leaves HBM once.  The row's kept blocks are walked in 16-key
-//   chunks through a software pipeline in which every operand reaches the
-//   matrix cores from LDS:
-//   * per chunk, the [H_s][16][16] tile slice (triple buffered) and the
-//     [H_kv][16 keys][128] slice of the prepared V (double buffered) are
-//     copied HBM/L2 -> LDS with the gfx950 direct-to-LDS 16-byte loads, two
-//     chunks ahead, through asm wrappers with explicit counter waits: loads
-//     complete in issue order, so one wait per chunk (for the V slice about
-//     to be used) also covers the next tile slice, and no barrier drains the
-//     prefetch;
-//   * head mix on MFMA 16x16x32 (M = 16 receiver heads, K = sender heads,
-//     N = 16 tile positions); each wavefront owns one M tile and 8 rows.  B
-//     operands are 16-byte LDS runs of 8 sender heads, transposed in
-//     registers (v_perm_b32).  bf16 tiles use bf16 MFMA with W split into
-//     hi + lo bf16 halves (W enters exactly, tiles need no conversion; the lo
-//     half of a partly filled K step rides in its empty K slots); fp16 tiles
-//     use fp16 MFMA with W in fp16;
-//   * the fp32 mixed map is rounded to fp16 into a swizzled LDS tile, which is
-//     also the re-layout to "query rows across lanes, keys along K";
-//   * Ahat . V on MFMA 32x32x16 f16 with M = two receiver heads of one KV
-//     group x 16 rows (16x16x16 when receivers cannot be paired inside a
-//     group), N = 32 head-dim columns, K = the chunk's 16 keys;
-//   * accumulators (16 rows x RPW heads x 128 d per wavefront) stay in AGPRs
-//     for the whole row; O is written once through an LDS transpose as
-//     16-byte stores.
-//   Blocks of consecutive rows go to one XCD, so the V slices of their shared
+// k_retrieve_mfma (fp16/bf16, d = 128, B in {16,32,64,128}, H_r in
+//                  {8,16,24,32}, H_s <= 48, each wavefront's receivers in
+//                  one KV group)
+//   Work item = (block row I, 16-row slice); one 512-thread workgroup (eight
+//   wavefronts, two per SIMD) owns all receiver heads and all of d for its 16
+//   query rows, so every kept tile element leaves HBM once.  The row's kept
+//   blocks are walked in 16-key chunks.  Phase u of the loop, between two
+//   workgroup barriers, does
+//     * A.V of chunk u: MFMA 32x32x16 with M = two receiver heads x 16 rows,
+//       N = 32 head-dim columns, K = the chunk's 16 keys, accumulating in
+//       registers for the whole row (wavefront w owns receivers
+//       [w*H_r/8, (w+1)*H_r/8), which share one KV head);
+//     * head mix of chunk u+1: MFMA 16x16x32 with M = 16 receiver heads,
+//       K = sender heads, N = 16 (row, key) positions; each wavefront owns one
+//       M tile and 4 rows; the fp32 result goes to a double-buffered LDS tile
+//       in the A.V operand layout;
+//     * loads: the V rows of chunk u+1 straight into registers (8-byte loads
+//       from V's own row layout, transposed in registers so that each lane
+//       holds eight consecutive keys of four head-dim columns), then the
+//       [H_s][16 rows][16 keys] tile slice of chunk u+3 into LDS with the
+//       gfx950 direct-to-LDS 16-byte loads (three slices in flight).
+//   Loads return in issue order, so one counter wait per phase ("all but the
+//   newest tile slice") covers both the V registers and the slice needed
+//   next; no barrier drains the prefetch.
+//   bf16: the head mix runs on bf16 MFMA with W split into hi + lo bf16 halves
+//   (W enters exactly); the fp32 mixed map is split the same way into hi + lo
+//   bf16 planes, and A.V runs on bf16 MFMA for both planes against the bf16 V
+//   as stored, so nothing is rounded except the mixed map's hi + lo split
+//   (16 significant bits).  fp16: W and the mixed map are rounded to fp16, V
+//   is used as stored.
+//   Blocks of consecutive rows go to one XCD, so the V rows of their shared
 //   band columns stay in that XCD's L2.
 //
 // k_retrieve_simple (every other supported case, including fp32)
 //   One workgroup per (block row, receiver head): the mixed tile is built in
 //   LDS in fp32, then multiplied with V by plain fp32 FMAs.
 #include <algorithm>
-#include <type_traits>
 
 #include "mf_internal.h"
 
@@ -66,37 +55,34 @@ namespace {
 using namespace mfd;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kD = 128;          // head dim of the MFMA kernel
-constexpr int kRows = 16;        // query rows per work item
-constexpr int kCB = 16;          // keys per pipeline chunk
-constexpr int kMaxRecv = 32;     // receiver heads of the MFMA kernel
-constexpr int kMaxHs = 48;       // sender heads of the MFMA kernel
-constexpr int kMaxKV = 8;        // KV heads of the MFMA kernel
-constexpr int kHeadSlot = kRows * kCB * 2;        // bytes: one head of one chunk
-constexpr int kVSlot = kMaxKV * kCB * kD * 2;     // bytes: V slice of one chunk
-constexpr int kAhatBytes = kMaxRecv * kRows * kCB * 2;
-constexpr int kVDma = kVSlot / 1024 / 4;          // V copies per wavefront per chunk
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;          // MFMA kernel workgroup
+constexpr int kSimpleThreads = 256;            // plain kernel workgroup
+constexpr int kD = 128;                        // head dim of the MFMA kernel
+constexpr int kRows = 16;                      // query rows per work item
+constexpr int kCB = 16;                        // keys per pipeline chunk
+constexpr int kMaxRecv = 32;                   // receiver heads of the MFMA kernel
+constexpr int kMaxHs = 48;                     // sender heads of the MFMA kernel
+constexpr int kHeadSlot = kRows * kCB * 2;     // bytes: one head of one tile slice
+constexpr int kPlane = kMaxRecv * kRows * kCB * 2;  // bytes: one mixed-map plane
+constexpr int kOutSlot = 2 * kRows * kD * 2;   // bytes: a receiver pair's output rows
 
 __device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ f16x4 as_f16x4(const uint2& v) { return __builtin_bit_cast(f16x4, v); }
 
-// 8x8 transpose of 16-bit elements held as 8 rows of 8 (u32x4 each):
+// 8x4 transpose of 16-bit elements held as 8 rows of 4 (u32x2 each):
 // out[t] element j = in[j] element t.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8]) {
+__device__ __forceinline__ void transpose8x4(const u32x2 (&x)[8], u32x4 (&y)[4]) {
   constexpr unsigned kLo = 0x05040100u;  // low halves of (src1, src0)
   constexpr unsigned kHi = 0x07060302u;  // high halves of (src1, src0)
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const unsigned sel = (t & 1) ? kHi : kLo;
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      y[t][m] = __builtin_amdgcn_perm(x[2 * m + 1][t >> 1], x[2 * m][t >> 1], sel);
-  }
+      y[t][m] = __builtin_amdgcn_perm(x[2 * m + 1][t >> 1], x[2 * m][t >> 1], (t & 1) ? kHi : kLo);
 }
 
 // The retrieval loop issues its vector-memory traffic through these wrappers
@@ -108,10 +94,23 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
 }
+__device__ __forceinline__ void gload8(u32x2& r, const void* g) {
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(g) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// Same wait; the registers of an asm load are tied to it, so no use of them
+// can be scheduled before the data has arrived.
+template <int N>
+__device__ __forceinline__ void wait_vm_tied(u32x2 (&r)[8]) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]),
+                 "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
+               : "n"(N) : "memory");
 }
 // Workgroup barrier for LDS traffic only (outstanding memory loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
@@ -124,71 +123,6 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 
 __device__ __forceinline__ unsigned short bf16_bits(float f) {
   return __builtin_bit_cast(unsigned short, (__bf16)f);  // RNE
-}
-
-// ---------------------------------------------------------------------------
-// V preparation: one workgroup per (64 keys, KV head)
-// ---------------------------------------------------------------------------
-
-template <bool kBF16, bool kVec>
-__global__ __launch_bounds__(kThreads) void k_prep_values(
-    const unsigned short* __restrict__ V, int N, int H_kv, int64_t ldV, int nkey8,
-    unsigned short* __restrict__ Vp, int* __restrict__ escale) {
-  __shared__ unsigned short tile[64][kD + 2];
-  const int k0 = blockIdx.x * 64;
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int key = k0 + (tid >> 2);      // one key per 4 threads, 32 d each
-  const int dq = (tid & 3) * 32;
-  float v[32];
-  if (key < N) {
-    const unsigned short* src = V + (int64_t)key * ldV + (int64_t)g * kD + dq;
-    if constexpr (kVec) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const unsigned short lo = w[e] & 0xffffu, hi = w[e] >> 16;
-          v[8 * j + 2 * e] = kBF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
-          v[8 * j + 2 * e + 1] = kBF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) v[e] = kBF16 ? bf16_to_f32(src[e]) : f16_to_f32(src[e]);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) v[e] = 0.f;
-  }
-  // per 16-key chunk (= one wavefront) range scale
-  float mx = 0.f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  int ex = 0;
-  if (kBF16 && mx >= 32768.f) {
-    int x;
-    frexpf(mx, &x);                     // mx < 2^x
-    ex = min(x - 15, 120);
-  }
-#pragma unroll
-  for (int e = 0; e < 32; ++e) tile[tid >> 2][dq + e] = f32_to_f16(__builtin_ldexpf(v[e], -ex));
-  if ((tid & 63) == 0) escale[(int64_t)(k0 / kCB + (tid >> 6)) * H_kv + g] = ex;
-  __syncthreads();
-  // Vp[g][key/8][d][8]: thread -> (8-key group, d), 4 per thread
-#pragma unroll
-  for (int rep = 0; rep < 4; ++rep) {
-    const int e = tid + rep * kThreads;
-    const int c8 = e >> 7, dd = e & (kD - 1);
-    u32x4 pk;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      pk[j] = (unsigned)tile[8 * c8 + 2 * j][dd] | ((unsigned)tile[8 * c8 + 2 * j + 1][dd] << 16);
-    const int64_t row8 = (int64_t)g * nkey8 + k0 / 8 + c8;
-    *reinterpret_cast<u32x4*>(Vp + (row8 * kD + dd) * 8) = pk;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -237,30 +171,30 @@ struct HmPlan {
   }
 };
 
-// RPW receiver heads per wavefront (H_r = 4 * RPW); GS consecutive receivers
-// share one KV group inside a wavefront (GS = G when a wavefront spans two
-// groups, GS = RPW when it lies inside one): local receiver rl reads group
-// g0 + rl / GS.  With GS even, receivers are paired for the 32x32 A.V.
-template <bool kBF16, int NCH, int RPW, int GS>
+// NPAIR = ceil(RPW / 2) receiver pairs per wavefront, RPW = H_r / 8 receivers
+// (a pair's second receiver past RPW is computed from valid data and never
+// stored).  lg_ncc = log2(B / 16).
+template <bool kBF16, int NCH, int NPAIR>
 __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N,
-    int B, const float* __restrict__ W, int H_r,
-    const unsigned short* __restrict__ Vp, const int* __restrict__ escale,
-    int nkey8, int H_kv, unsigned short* __restrict__ O, int64_t ldO, int RG) {
+    const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N, int B,
+    int lg_ncc, const float* __restrict__ W, int H_r, int RPW, int G,
+    const unsigned short* __restrict__ V, int64_t ldV,
+    unsigned short* __restrict__ O, int64_t ldO, int RG) {
   using Plan = HmPlan<kBF16, NCH>;
   constexpr int NBOP = Plan::NBOP;
-  constexpr int MT = RPW > 4 ? 2 : 1;             // 16-receiver M tiles of the head mix
-  constexpr bool kPairs = (GS % 2) == 0;          // 32x32x16 A.V on receiver pairs
-  constexpr int NSTG = 3;                         // tile-slice buffers in flight
-  constexpr int kStage = 8 * NCH * kHeadSlot;     // one tile slice: head slots 0..8*NCH-1
-  constexpr int NDV = NCH;                        // tile-slice copies per wavefront per chunk
-  constexpr int kSmem = NSTG * kStage + 2 * kVSlot + kAhatBytes;
+  constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
+  constexpr int NSTG = 3;                          // tile-slice buffers
+  constexpr int kStage = 8 * NCH * kHeadSlot;      // one tile slice: head slots 0..8*NCH-1
+  constexpr int NPR = 4 * NCH;                     // 1 KB copies per tile slice
+  constexpr int NDV = (NPR + kWaves - 1) / kWaves; // copies per wavefront per slice
+  constexpr int kAhatOff = NSTG * kStage;
+  constexpr int kAhatBuf = NPL * kPlane;
+  constexpr int kUsed = kAhatOff + 2 * kAhatBuf;
+  constexpr int kSmem = kUsed > kWaves * kOutSlot ? kUsed : kWaves * kOutSlot;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
-  static_assert(RPW % GS == 0 && RPW / GS <= 2, "at most two KV groups per wavefront");
+  static_assert(NPAIR == 1 || NPAIR == 2, "receiver pairs per wavefront");
   __shared__ __align__(16) unsigned char smem[kSmem];
-  unsigned char* vstage = smem + NSTG * kStage;
-  unsigned short* Ahs = reinterpret_cast<unsigned short*>(smem + NSTG * kStage + 2 * kVSlot);
 
   const int T = (N + B - 1) / B;
   const int subs = B / kRows;
@@ -272,14 +206,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   const int n = lane & 15;
   const int q = lane >> 4;
 
-  // ---- head mix role: M tile hm_mt, tile rows 8*(wave&1)..+7 -------------
-  const int hm_mt = wave >> 1;
-  const bool hm_on = hm_mt < MT;
+  // ---- head-mix role: M tile hm_mt (receivers 16 hm_mt..+15), rows 4 rq..+3
+  const int hm_mt = wave >> 2;
+  const int rq = wave & 3;
   u32x4 wop[NBOP][2];
 #pragma unroll
   for (int b = 0; b < NBOP; ++b)
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < Plan::nw(b); ++w) {
       const int r = 16 * hm_mt + n;
       const int c = Plan::chunk(b, q);
       const int hf = Plan::half(b, w, q);
@@ -287,237 +221,225 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int s = 8 * c + j;
-        const float x = (w < Plan::nw(b) && c >= 0 && r < H_r && s < H_s) ? W[(int64_t)r * H_s + s] : 0.f;
-        if (kBF16) {
-          const unsigned short hi = bf16_bits(x);
-          hv[j] = hf == 0 ? hi : bf16_bits(x - bf16_to_f32(hi));
+        const bool ok = c >= 0 && r < H_r && s < H_s;
+        const float x = W[ok ? r * H_s + s : 0];       // unconditional: all loads in flight together
+        const float xv = ok ? x : 0.f;
+        if constexpr (kBF16) {
+          const unsigned short hi = bf16_bits(xv);
+          hv[j] = hf == 0 ? hi : bf16_bits(xv - bf16_to_f32(hi));
         } else {
-          hv[j] = f32_to_f16(x);
+          hv[j] = f32_to_f16(xv);
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) wop[b][w][j] = (unsigned)hv[2 * j] | ((unsigned)hv[2 * j + 1] << 16);
     }
+  // the W loads must have landed before the first counted asm load is issued
+#pragma unroll
+  for (int b = 0; b < NBOP; ++b) asm volatile("" :: "v"(wop[b][0]));
 
   // ---- accumulators ---------------------------------------------------------
-  constexpr int NACC = kPairs ? RPW / 2 : RPW;
-  constexpr int NDT = kPairs ? 4 : 8;
-  using AccT = typename std::conditional<kPairs, f32x16, f32x4>::type;
-  AccT acc[NACC][NDT];
+  f32x16 acc[NPAIR][4];
 #pragma unroll
-  for (int p = 0; p < NACC; ++p)
+  for (int p = 0; p < NPAIR; ++p)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[p][dt] = AccT{};
+    for (int dt = 0; dt < 4; ++dt) acc[p][dt] = f32x16{};
 
-  const int G = H_r / H_kv;
   const int rbeg = wave * RPW;
-  const int g0 = rbeg / G;
+  const int g = rbeg / G;
   int64_t kb = row_ptr[I], ke = row_ptr[I + 1];
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
-  const int ncc = B / kCB;
-  const int nchunks = (int)(ke - kb) * ncc;
-  const int64_t tile_elems = (int64_t)B * B;
+  const int ncc_mask = (1 << lg_ncc) - 1;
+  const int n_chunks = (int)(ke - kb) << lg_ncc;
+  const int64_t tile = (int64_t)B * B;
+  auto block_of = [&](int x) -> int64_t {       // kept block of chunk x (clamped)
+    x = x < n_chunks ? x : n_chunks - 1;
+    return kb + (x >> lg_ncc);
+  };
+  auto col_ok = [&](int J) { return J >= 0 && J < T; };
 
-  // chunk u -> (kept block k, 16-key column chunk cc, global 16-key chunk of V)
-  auto chunk_of = [&](int u, int64_t* k, int* cc, int* vch, bool* ok) {
-    *k = kb + u / ncc;
-    *cc = u % ncc;
-    const int J = col_idx[*k];
-    *ok = (J >= 0 && J < T);
-    *vch = *ok ? (J * B + *cc * kCB) / kCB : 0;
-  };
-  // tile slice: [H_s][16 rows][16 keys]; one copy = 2 heads x 16 rows x 32 bytes
-  const int lane_row = (lane & 31) >> 1;
-  const int lane_off = (sub * kRows + lane_row) * B + (lane & 1) * 8;
-  auto issue_vals = [&](int u) {
-    int64_t k; int cc, vch; bool ok;
-    chunk_of(u, &k, &cc, &vch, &ok);
-    const unsigned base = lds_addr(smem + (u % NSTG) * kStage);
-    const unsigned short* src0 = vals + k * H_s * tile_elems + lane_off + cc * kCB;
+  // tile-slice copy d of this wavefront: 1 KB piece pr = heads 2pr, 2pr+1;
+  // lane -> (head 2pr + lane/32, tile row (lane%32)/2, 16-byte half lane%2)
+  const int64_t lane_off = (int64_t)(sub * kRows + ((lane & 31) >> 1)) * B + (lane & 1) * 8;
+  int64_t head_off[NDV];
+  int piece[NDV];
 #pragma unroll
-    for (int m = 0; m < NDV; ++m) {
-      const int pair = wave + 4 * m;                    // heads 2*pair, 2*pair+1
-      int s = 2 * pair + (lane >> 5);
-      s = s < H_s ? s : H_s - 1;                        // padding slots get a real head (zero weight)
-      dma16(src0 + s * tile_elems, base + pair * 1024);
-    }
-  };
-  // V slice: [g][2 x 8 keys][128][8] = 4 KB per KV head, copied in 1 KB pieces
-  auto issue_v = [&](int u) {
-    int64_t k; int cc, vch; bool ok;
-    chunk_of(u, &k, &cc, &vch, &ok);
-    const unsigned base = lds_addr(vstage + (u & 1) * kVSlot);
-#pragma unroll
-    for (int m = 0; m < kVDma; ++m) {
-      const int piece = wave + 4 * m;                   // 0..31
-      int g = piece >> 2;
-      g = g < H_kv ? g : H_kv - 1;
-      const unsigned short* src =
-          Vp + ((int64_t)g * nkey8 + (int64_t)vch * 2) * kD * 8 + (piece & 3) * 512 + lane * 8;
-      dma16(src, base + piece * 1024);
-    }
-  };
-
-  constexpr int NDMA = NDV + kVDma;
-  // prologue: vals(0), vals(1), V(0), vals(2), V(1)  (the steady-state order)
-  if (nchunks > 0) issue_vals(0);
-  if (nchunks > 1) issue_vals(1);
-  if (nchunks > 0) issue_v(0);
-  if (nchunks > 2) issue_vals(2);
-  if (nchunks > 1) issue_v(1);
-  if (nchunks > 0) {
-    // vals(0) must have landed before the first head mix
-    if (nchunks > 2) wait_vm<2 * NDV + 2 * kVDma>();
-    else if (nchunks > 1) wait_vm<NDV + 2 * kVDma>();
-    else wait_vm<kVDma>();
-    lds_barrier();
+  for (int d = 0; d < NDV; ++d) {
+    const int pr = wave + kWaves * d < NPR ? wave + kWaves * d : NPR - 1;  // surplus copies repeat the last piece
+    int s = 2 * pr + (lane >> 5);
+    s = s < H_s ? s : H_s - 1;                  // padding slots get a real head (zero weight)
+    head_off[d] = s * tile + lane_off;
+    piece[d] = pr;
   }
-
-  const int hrow = 8 * (wave & 1) + (n >> 1);          // head-mix tile row of this lane
-  const int hcg = n & 1;                               // 8-key half of the chunk
-  for (int u = 0; u < nchunks; ++u) {
-    int64_t k; int cc, vch; bool jok;
-    chunk_of(u, &k, &cc, &vch, &jok);
-
-    // ---- head mix: M tile hm_mt, rows hrow, 16 keys -------------------------
-    if (hm_on) {
-      const unsigned short* buf = reinterpret_cast<const unsigned short*>(smem + (u % NSTG) * kStage);
-      f32x4 c[8];
+  const unsigned smem_lds = lds_addr(smem);
+  auto issue_vals = [&](int x, int slot) {
+    const int xc = x < n_chunks ? x : n_chunks - 1;
+    const unsigned short* src = vals + block_of(x) * H_s * tile + (xc & ncc_mask) * kCB;
+    const unsigned base = smem_lds + slot * kStage;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < NDV; ++d) dma16(src + head_off[d], base + piece[d] * 1024);
+  };
+  // V rows of chunk x: lane -> keys 8*(lane/32)..+7 of the chunk, head-dim
+  // columns 4*(lane%32)..+3 of KV head g (rows past N read row N-1, whose
+  // weight is zero)
+  const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
+  auto issue_v = [&](int x, int J, u32x2 (&vr)[8]) {
+    const int xc = x < n_chunks ? x : n_chunks - 1;
+    const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB + 8 * (lane >> 5);
 #pragma unroll
-      for (int b = 0; b < NBOP; ++b) {
-        // lane groups without a chunk read chunk 0; their W slots are zero
-        const int ch = Plan::chunk(b, q) < 0 ? 0 : Plan::chunk(b, q);
-        u32x4 x[8], y[8];
-#pragma unroll
-        for (int uu = 0; uu < 8; ++uu)
-          x[uu] = *reinterpret_cast<const u32x4*>(buf + ((8 * ch + uu) * kRows + hrow) * kCB + hcg * 8);
-        transpose8x8(x, y);
-#pragma unroll
-        for (int w = 0; w < Plan::nw(b); ++w)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            if constexpr (kBF16)
-              c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wop[b][w]), as_bf16x8(y[t]), c[t], 0, 0, 0);
-            else
-              c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wop[b][w]), as_f16x8(y[t]), c[t], 0, 0, 0);
-          }
-      }
-      // lane (n, q) holds Ahat[16 hm_mt + 4q + a][hrow][8 hcg + t]; rows of Ahs
-      // are 32 bytes, their two 16-byte halves swapped on rows 8..15
-      // a block with an invalid column contributes nothing: its mixed map is
-      // zeroed (the A.V below runs unconditionally on a valid V slice)
-      int scale_any = 0;
-      if (jok)
-        for (int g = 0; g < H_kv; ++g) scale_any |= escale[(int64_t)vch * H_kv + g];
-      const float zero_if_bad = jok ? 1.f : 0.f;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = 16 * hm_mt + 4 * q + a;
-        if (r < H_r) {
-          const float sc = scale_any ? __builtin_ldexpf(1.f, escale[(int64_t)vch * H_kv + r / G])
-                                     : zero_if_bad;
-          u32x4 pk;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pk[j] = pack_f16x2(c[2 * j][a] * sc, c[2 * j + 1][a] * sc);
-          *reinterpret_cast<u32x4*>(&Ahs[(r * kRows + hrow) * kCB + 8 * (hcg ^ (hrow >> 3))]) = pk;
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int key = key0 + j < N ? key0 + j : N - 1;
+      gload8(vr[j], vlane + (int64_t)key * ldV);
     }
-    // V(u) landed (and, being issued later, vals(u+1) too)
-    if (u + 2 < nchunks) wait_vm<NDV + kVDma>();
-    else if (u + 1 < nchunks) wait_vm<kVDma>();
-    else wait_vm<0>();
-    lds_barrier();
-    if (u + 3 < nchunks) issue_vals(u + 3);
+  };
 
-    // ---- Ahat . V -------------------------------------------------------------
-    {
-      const unsigned char* vb = vstage + (u & 1) * kVSlot;
-      if constexpr (kPairs) {
-        const int m = lane & 31, hh = lane >> 5;
-        const int rp = m >> 4, i = m & 15;
-        u32x4 bop[2][4];
+  // head mix of chunk x from tile slot `slot` into mixed-map buffer `ab`;
+  // `keep` = 0 zeroes the chunk (invalid column or padding chunk)
+  const int hrow = 4 * rq + (n >> 2);            // tile row of this lane
+  const int hkq = n & 3;                         // 4-key quarter of the chunk
+  const int hm_off = hrow * 32 + (((hkq >> 1) ^ ((hrow >> 2) & 1)) * 16) + (hkq & 1) * 8;
+  auto head_mix = [&](int slot, bool keep, int ab) {
+    const unsigned char* st = smem + slot * kStage + hrow * 32 + hkq * 8;
+    f32x4 c[4];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int g = min(g0 + gi, H_kv - 1);
+    for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            bop[gi][dt] = *reinterpret_cast<const u32x4*>(vb + ((g * 2 + hh) * kD + 32 * dt + m) * 16);
+    for (int b = 0; b < NBOP; ++b) {
+      // lane groups without a chunk read chunk 0; their W slots are zero
+      const int ch = Plan::chunk(b, q) < 0 ? 0 : Plan::chunk(b, q);
+      u32x2 x[8];
+      u32x4 y[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[j] = *reinterpret_cast<const u32x2*>(st + (8 * ch + j) * kHeadSlot);
+      transpose8x4(x, y);
+#pragma unroll
+      for (int w = 0; w < Plan::nw(b); ++w)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (kBF16)
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wop[b][w]), as_bf16x8(y[t]), c[t], 0, 0, 0);
+          else
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wop[b][w]), as_f16x8(y[t]), c[t], 0, 0, 0);
         }
+    }
+    // lane (n, q) holds Ahat[16 hm_mt + 4q + a][hrow][4 hkq + t]; a plane is
+    // [32 receivers][16 rows][16 keys], its rows' two 16-byte halves swapped
+    // when bit 2 of the row is set
+    const float sc = keep ? 1.f : 0.f;
+    unsigned char* dst = smem + kAhatOff + ab * kAhatBuf + hm_off;
 #pragma unroll
-        for (int p = 0; p < NACC; ++p) {
-          const int r = rbeg + 2 * p + rp;
-          const u32x4 a4 = *reinterpret_cast<const u32x4*>(&Ahs[(r * kRows + i) * kCB + 8 * (hh ^ (i >> 3))]);
+    for (int a = 0; a < 4; ++a) {
+      const int r = 16 * hm_mt + 4 * q + a;
+      float v[4];
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                as_f16x8(a4), as_f16x8(bop[(2 * p) / GS][dt]), acc[p][dt], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) v[t] = c[t][a] * sc;
+      if constexpr (kBF16) {
+        unsigned short hi[4], lo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          hi[t] = bf16_bits(v[t]);
+          lo[t] = bf16_bits(v[t] - bf16_to_f32(hi[t]));
         }
+        *reinterpret_cast<u32x2*>(dst + r * 512) =
+            u32x2{(unsigned)hi[0] | ((unsigned)hi[1] << 16), (unsigned)hi[2] | ((unsigned)hi[3] << 16)};
+        *reinterpret_cast<u32x2*>(dst + kPlane + r * 512) =
+            u32x2{(unsigned)lo[0] | ((unsigned)lo[1] << 16), (unsigned)lo[2] | ((unsigned)lo[3] << 16)};
       } else {
-        uint2 bop[2][8];
+        *reinterpret_cast<u32x2*>(dst + r * 512) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+      }
+    }
+  };
+
+  // A.V of the chunk whose mixed map is in buffer `ab` and V rows in `vr`
+  const int am = lane & 31;
+  const int a_off = (am & 15) * 32 + (((lane >> 5) ^ ((am >> 2) & 1)) * 16);
+  auto a_dot_v = [&](int ab, const u32x2 (&vr)[8]) {
+    u32x4 vt[4];                                 // vt[dt]: 8 keys of column 4*(lane%32)+dt
+    transpose8x4(vr, vt);
+    const unsigned char* src = smem + kAhatOff + ab * kAhatBuf + a_off;
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int g = min(g0 + gi, H_kv - 1);
+    for (int p = 0; p < NPAIR; ++p) {
+      const int r = rbeg + 2 * p + (am >> 4);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            bop[gi][dt] = *reinterpret_cast<const uint2*>(
-                vb + ((g * 2 + (q >> 1)) * kD + 16 * dt + n) * 16 + (q & 1) * 8);
-        }
+      for (int pl = 0; pl < NPL; ++pl) {
+        const u32x4 a4 = *reinterpret_cast<const u32x4*>(src + pl * kPlane + r * 512);
 #pragma unroll
-        for (int rl = 0; rl < RPW; ++rl) {
-          const int r = rbeg + rl;
-          const uint2 a2 = *reinterpret_cast<const uint2*>(
-              &Ahs[(r * kRows + n) * kCB + 8 * ((q >> 1) ^ (n >> 3)) + 4 * (q & 1)]);
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            acc[rl][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                as_f16x4(a2), as_f16x4(bop[rl / GS][dt]), acc[rl][dt], 0, 0, 0);
+        for (int dt = 0; dt < 4; ++dt) {
+          if constexpr (kBF16)
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a4), as_bf16x8(vt[dt]), acc[p][dt], 0, 0, 0);
+          else
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a4), as_f16x8(vt[dt]), acc[p][dt], 0, 0, 0);
         }
       }
     }
-    lds_barrier();
-    if (u + 2 < nchunks) issue_v(u + 2);
-  }
+  };
 
-  // ---- store through LDS: one receiver head at a time per wavefront --------
-  unsigned short* ot = reinterpret_cast<unsigned short*>(smem) + wave * (kRows * kD);
-#pragma unroll
-  for (int rl = 0; rl < RPW; ++rl) {
-    const int r = rbeg + rl;
+  // ---- pipeline ---------------------------------------------------------------
+  // phase u: issue V(u+1) and tile slice u+3, A.V(u), head mix(u+1), wait, barrier
+  u32x2 vA[8], vB[8];
+  int J1 = 0;                                    // column of chunk u+1
+  if (n_chunks > 0) {
+    const int J0 = col_idx[block_of(0)];
+    J1 = col_idx[block_of(1)];
+    issue_v(0, J0, vA);
+    issue_vals(0, 0);
+    issue_vals(1, 1);
+    issue_vals(2, 2);
+    wait_vm_tied<2 * NDV>(vA);                   // V(0) and slice 0 landed
     lds_barrier();
-    if constexpr (kPairs) {
-      // acc[rl/2][dt][e]: row m = 8(e>>2) + 4(lane>>5) + (e&3) of the pair,
-      // receiver m>>4, tile row m&15, column d = 32 dt + (lane&31)
+    head_mix(0, col_ok(J0), 0);
+    wait_vm<NDV>();                              // slice 1 landed
+    lds_barrier();
+  }
+  const int n_pad = (n_chunks + 1) & ~1;
+  int slot = 0;                                  // u % 3
+  auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8]) {
+    const int Jn = col_idx[block_of(u + 2)];
+    issue_v(u + 1, J1, vnext);
+    issue_vals(u + 3, slot);
+    a_dot_v(u & 1, vcur);
+    const int s1 = slot == 2 ? 0 : slot + 1;
+    head_mix(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1);
+    wait_vm_tied<NDV>(vnext);                    // V(u+1) and slice u+2 landed
+    lds_barrier();
+    J1 = Jn;
+    slot = s1;
+  };
+  for (int u = 0; u < n_pad; u += 2) {
+    phase(u, vA, vB);
+    phase(u + 1, vB, vA);
+  }
+  wait_vm<0>();
+  lds_barrier();
+
+  // ---- store through LDS: one receiver pair at a time per wavefront ---------
+  unsigned short* ot = reinterpret_cast<unsigned short*>(smem + wave * kOutSlot);  // [16 rows][2][128]
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+  for (int p = 0; p < NPAIR; ++p) {
+    if (p) lds_barrier();
+    // acc[p][dt][e]: row m = 8(e>>2) + 4(lane>>5) + (e&3) of the pair (receiver
+    // m>>4, tile row m&15), head-dim column 4 (lane&31) + dt
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if ((m >> 4) == (rl & 1)) {
-            const float v = acc[rl >> 1][dt][e];
-            ot[(m & 15) * kD + 32 * dt + (lane & 31)] = kBF16 ? bf16_bits(v) : f32_to_f16(v);
-          }
-        }
-    } else {
+    for (int e = 0; e < 16; ++e) {
+      const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      unsigned short h[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float v = acc[rl][dt][a];
-          ot[(4 * q + a) * kD + 16 * dt + n] = kBF16 ? bf16_bits(v) : f32_to_f16(v);
-        }
+      for (int dt = 0; dt < 4; ++dt) h[dt] = kBF16 ? bf16_bits(acc[p][dt][e]) : f32_to_f16(acc[p][dt][e]);
+      *reinterpret_cast<u32x2*>(ot + ((m & 15) * 2 + (m >> 4)) * kD + 4 * am) =
+          u32x2{(unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16)};
     }
     lds_barrier();
-    // each lane stores 16 contiguous bytes: row lane/16 + 4*pass, d = 8*(lane%16)
+    // 16 rows x 2 receivers x 256 bytes, 16 contiguous bytes per lane
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int i = 4 * pass + (lane >> 4);
+    for (int pass = 0; pass < 8; ++pass) {
+      const int c16 = pass * 64 + lane;
+      const int i = c16 >> 5, rp = (c16 >> 4) & 1, d8 = (c16 & 15) * 8;
       const int64_t grow = (int64_t)I * B + sub * kRows + i;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&ot[i * kD + 8 * n]);
-      if (grow < N) *reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)r * kD + 8 * n) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + (i * 2 + rp) * kD + d8);
+      if (2 * p + rp < RPW && grow < N)
+        *reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)(rbeg + 2 * p + rp) * kD + d8) = v;
     }
   }
 }
@@ -527,12 +449,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 // ---------------------------------------------------------------------------
 
 template <class TT, int BB, int D>
-__global__ __launch_bounds__(kThreads) void k_retrieve_simple(
+__global__ __launch_bounds__(kSimpleThreads) void k_retrieve_simple(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const typename TT::S* __restrict__ vals, int64_t nnzb, int H_s, int N,
     const float* __restrict__ W, int H_r, const typename TT::S* __restrict__ V,
     int H_kv, int64_t ldV, typename TT::S* __restrict__ O, int64_t ldO) {
-  constexpr int RPP = kThreads / D;        // query rows per pass
+  constexpr int RPP = kSimpleThreads / D;        // query rows per pass
   constexpr int NACC = BB / RPP;           // rows per thread
   __shared__ float ahat[BB * BB];
   __shared__ float wrow[64];
@@ -555,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_retrieve_simple(
     const int J = col_idx[k];
     if (J < 0 || J >= T) continue;
     const typename TT::S* blk = vals + k * H_s * BB * BB;
-    for (int e = tid; e < BB * BB; e += kThreads) {
+    for (int e = tid; e < BB * BB; e += kSimpleThreads) {
       float s = 0.f;
       for (int h = 0; h < H_s; ++h) s += wrow[h] * TT::tof(blk[(int64_t)h * BB * BB + e]);
       ahat[e] = s;
@@ -583,7 +505,7 @@ int launch_simple_t(const int32_t* row_ptr, const int32_t* col_idx, const void* 
                     hipStream_t st) {
   using S = typename TT::S;
   const int T = mf::blocks_of(N, BB);
-  hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D>), dim3(T, H_r), dim3(kThreads),
+  hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D>), dim3(T, H_r), dim3(kSimpleThreads),
                      0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
                      nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
                      ldV, reinterpret_cast<S*>(O), ldO);
@@ -613,36 +535,19 @@ int launch_simple(int B, int d, const int32_t* row_ptr, const int32_t* col_idx,
   return launch_simple_d<TT, 128>(B, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
 }
 
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Workspace layout of the MFMA path: Vp | escale (each 256-byte aligned).
-struct WsLayout {
-  size_t vp, es, total;
-  int nkey8;      // 8-key rows of Vp per KV head (covers T*B keys, a multiple of 64)
-};
-inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline WsLayout ws_layout(int N, int B, int H_kv) {
-  WsLayout L;
-  const int T = mf::blocks_of(N, B);
-  const int keys = ((T * B + 63) / 64) * 64;
-  L.nkey8 = keys / 8;
-  L.vp = 0;
-  L.es = up256((size_t)H_kv * keys * kD * 2);
-  L.total = L.es + up256((size_t)(keys / kCB) * H_kv * 4);
-  return L;
-}
-
-template <bool kBF16, int RPW, int GS>
-int launch_mfma_g(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
+template <bool kBF16, int NPAIR>
+int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
                   const int32_t* col_idx, const unsigned short* vals, int64_t nnzb,
-                  int H_s, int N, int B, const float* W, int H_r,
-                  const unsigned short* Vp, const int* es, int nkey8, int H_kv,
-                  unsigned short* O, int64_t ldO, int RG) {
-#define MF_CASE(NCH_)                                                                     \
-  case NCH_:                                                                              \
-    hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, RPW, GS>), grid, dim3(kThreads), 0, \
-                       st, row_ptr, col_idx, vals, nnzb, H_s, N, B, W, H_r, Vp, es,       \
-                       nkey8, H_kv, O, ldO, RG);                                          \
+                  int H_s, int N, int B, int lg_ncc, const float* W, int H_r, int RPW,
+                  int G, const unsigned short* V, int64_t ldV, unsigned short* O,
+                  int64_t ldO, int RG) {
+#define MF_CASE(NCH_)                                                                      \
+  case NCH_:                                                                               \
+    hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR>), grid, dim3(kThreads), 0, st, \
+                       row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,    \
+                       V, ldV, O, ldO, RG);                                                \
     break;
   switch (NCH) {
     MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5) MF_CASE(6)
@@ -652,83 +557,49 @@ int launch_mfma_g(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
   return mf::hip_check(hipGetLastError(), "k_retrieve_mfma launch");
 }
 
-// Receiver split per wavefront: returns GS (receivers per KV-group segment
-// inside a wavefront) for the built (RPW, GS) pairs, 0 otherwise.
-inline int mfma_group_split(int H_r, int H_kv) {
-  if (H_r % 4 != 0) return 0;
-  const int rpw = H_r / 4, G = H_r / H_kv;
-  if (rpw != 2 && rpw != 4 && rpw != 6 && rpw != 8) return 0;
-  if (rpw % G == 0 && rpw / G <= 2) return G;   // whole groups, one or two of them
-  if (G % rpw == 0) return rpw;                  // inside one group
-  return 0;
-}
-
-template <bool kBF16>
-int launch_mfma(int NCH, int RPW, int GS, dim3 grid, hipStream_t st, const int32_t* row_ptr,
-                const int32_t* col_idx, const unsigned short* vals, int64_t nnzb, int H_s,
-                int N, int B, const float* W, int H_r, const unsigned short* Vp,
-                const int* es, int nkey8, int H_kv, unsigned short* O, int64_t ldO, int RG) {
-#define MF_G(R_, S_)                                                                    \
-  if (RPW == R_ && GS == S_)                                                            \
-    return launch_mfma_g<kBF16, R_, S_>(NCH, grid, st, row_ptr, col_idx, vals, nnzb,   \
-                                        H_s, N, B, W, H_r, Vp, es, nkey8, H_kv, O, ldO, \
-                                        RG);
-  MF_G(8, 4) MF_G(8, 8) MF_G(6, 3) MF_G(6, 6) MF_G(4, 2) MF_G(4, 4) MF_G(2, 1) MF_G(2, 2)
-#undef MF_G
-  return mf::fail(MF_ERR_UNSUPPORTED, "k_retrieve_mfma: receiver/KV-head split not built");
-}
-
 }  // namespace
 
 namespace mf {
 
+// The MFMA kernel covers fp16/bf16 with d = 128, B in {16, 32, 64, 128},
+// H_r in {8, 16, 24, 32}, H_s <= 48, the H_r/8 receivers of every wavefront
+// inside one KV group (G % (H_r/8) == 0), 16-byte aligned vals and O rows and
+// 8-byte aligned V rows.
 bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const void* vals,
-                        const void* O, int64_t ldO) {
-  return dt != MF_F32 && d == kD && B >= 32 && H_r <= kMaxRecv && H_s <= kMaxHs &&
-         H_kv <= kMaxKV && mfma_group_split(H_r, H_kv) > 0 && aligned16(vals) &&
-         aligned16(O) && (ldO % 8) == 0;
+                        const void* V, int64_t ldV, const void* O, int64_t ldO) {
+  if (dt == MF_F32 || d != kD || H_s > kMaxHs) return false;
+  if (B != 16 && B != 32 && B != 64 && B != 128) return false;
+  if (H_r % 8 != 0 || H_r > kMaxRecv) return false;
+  const int G = H_r / H_kv, RPW = H_r / 8;
+  if (G % RPW != 0) return false;
+  return aligned(vals, 16) && aligned(O, 16) && ldO % 8 == 0 && aligned(V, 8) && ldV % 4 == 0;
 }
 
-size_t retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dt) {
-  if (dt == MF_F32 || d != kD || B < 32) return 0;
-  return ws_layout(N, B, H_kv).total;
-}
+size_t retrieve_workspace_bytes(int, int, int, int, int) { return 0; }
 
 int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     const void* vals, int64_t nnzb, int dt, int H_s, int N,
                     int B, const float* W, int H_r, const void* V, int H_kv,
-                    int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
-                    size_t workspace_bytes, hipStream_t st) {
-  if (retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, O, ldO) && workspace &&
-      workspace_bytes >= ws_layout(N, B, H_kv).total) {
-    const WsLayout L = ws_layout(N, B, H_kv);
-    unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-    auto Vp = reinterpret_cast<unsigned short*>(ws + L.vp);
-    auto es = reinterpret_cast<int*>(ws + L.es);
-    auto Vs = reinterpret_cast<const unsigned short*>(V);
-    const bool vec = aligned16(V) && (ldV % 8) == 0;
-    const dim3 pgrid(L.nkey8 / 8, H_kv);
-    if (dt == MF_BF16) {
-      if (vec) hipLaunchKernelGGL((k_prep_values<true, true>), pgrid, dim3(kThreads), 0, st, Vs, N, H_kv, ldV, L.nkey8, Vp, es);
-      else hipLaunchKernelGGL((k_prep_values<true, false>), pgrid, dim3(kThreads), 0, st, Vs, N, H_kv, ldV, L.nkey8, Vp, es);
-    } else {
-      if (vec) hipLaunchKernelGGL((k_prep_values<false, true>), pgrid, dim3(kThreads), 0, st, Vs, N, H_kv, ldV, L.nkey8, Vp, es);
-      else hipLaunchKernelGGL((k_prep_values<false, false>), pgrid, dim3(kThreads), 0, st, Vs, N, H_kv, ldV, L.nkey8, Vp, es);
-    }
-    int rc = hip_check(hipGetLastError(), "k_prep_values launch");
-    if (rc != MF_OK) return rc;
+                    int d, int64_t ldV, void* O, int64_t ldO, void*, size_t,
+                    hipStream_t st) {
+  if (retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO)) {
     const int T = blocks_of(N, B);
     const int RG = std::max(1, T / 16);
     const int groups = (T + RG - 1) / RG;
     const int rows_per_xcd = ((groups + 7) / 8) * RG;
     const dim3 grid(rows_per_xcd * 8 * (B / kRows));
     const int NCH = (H_s + 7) / 8;
-    const int RPW = H_r / 4, GS = mfma_group_split(H_r, H_kv);
+    const int RPW = H_r / 8, G = H_r / H_kv;
+    const int lg_ncc = B == 16 ? 0 : B == 32 ? 1 : B == 64 ? 2 : 3;
     auto vp = reinterpret_cast<const unsigned short*>(vals);
+    auto Vs = reinterpret_cast<const unsigned short*>(V);
     auto Op = reinterpret_cast<unsigned short*>(O);
-    if (dt == MF_BF16)
-      return launch_mfma<true>(NCH, RPW, GS, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, W, H_r, Vp, es, L.nkey8, H_kv, Op, ldO, RG);
-    return launch_mfma<false>(NCH, RPW, GS, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, W, H_r, Vp, es, L.nkey8, H_kv, Op, ldO, RG);
+    const bool bf = dt == MF_BF16;
+    if (RPW > 2)
+      return bf ? launch_mfma_p<true, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG)
+                : launch_mfma_p<false, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG);
+    return bf ? launch_mfma_p<true, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG)
+              : launch_mfma_p<false, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG);
   }
   if (dt == MF_F32)
     return launch_simple<mfd::TF32>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);

@@ -128,12 +128,10 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
                        int64_t* nnzb_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mf_retrieve_fused needs for (N, B, H_kv, d, dtype); 0 when
- * the call needs none (fp32, d = 64 or B = 16).  It holds an fp16 copy of V
- * laid out for the matrix cores (H_kv * K * d * 2 bytes, K = ceil(N/B)*B
- * rounded up to a multiple of 64 keys, zero past N) plus one 4-byte
- * power-of-two range scale per 16-key chunk and KV head, each part aligned
- * to 256 bytes. */
+/* Workspace bytes mf_retrieve_fused needs for (N, B, H_kv, d, dtype).  The
+ * current kernels need none and return 0 for every configuration; the
+ * argument pair stays in mf_retrieve_fused so that a kernel which does need
+ * scratch can be added without changing the boundary. */
 size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
 
 /*
@@ -158,13 +156,13 @@ size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
  *            tensor): V[n][g][e] at V[n*ldV + g*d + e], n < N.
  *  O         device, O[n][r][e] at O[n*ldO + r*d + e], ldO >= H_r*d.
  *  workspace device scratch of >= mf_retrieve_workspace_bytes(...) bytes
- *            (may be NULL when that is 0); overwritten by the call.
- *  Precision: for MF_F16 and MF_BF16 the head mix runs on fp16 (bf16 for bf16
- *  maps, with W split into two bf16 halves so W enters exactly) matrix cores
- *  with fp32 accumulation; the mixed map is rounded to fp16 and multiplied
- *  with an fp16 copy of V (exact for bf16 values in [2^-17, 2^15]; larger
- *  values are scaled by a power of two per 16-key chunk).  MF_F32 runs in
- *  fp32 throughout.
+ *            (NULL when that is 0, as it is for every current kernel).
+ *  Precision: MF_F32 runs in fp32 throughout.  MF_BF16: the head mix runs on
+ *  bf16 matrix cores with W split into two bf16 halves (W enters exactly) and
+ *  fp32 accumulation; the fp32 mixed map is split the same way into hi + lo
+ *  bf16 parts, each multiplied with V as stored on bf16 matrix cores with
+ *  fp32 accumulation.  MF_F16: W and the mixed map are rounded to fp16 and
+ *  multiplied on fp16 matrix cores with fp32 accumulation.
  *  Errors: MF_ERR_INVALID for null pointers, N < 1, nnzb < 0, bad B, d not
  *  in {64,128}, H_s/H_r not in [1,64], H_kv < 1, H_r % H_kv != 0, ldV or ldO
  *  too small, a missing or short workspace, unknown dtype.

@@ -49,9 +49,11 @@ def test_version_and_status_strings(L):
 
 
 def test_retrieve_workspace_size(L):
-    n = mf.retrieve_workspace_bytes(8192, 64, 8, 128, __import__("torch").bfloat16)
-    assert n >= 8 * 8192 * 128 * 2 and n % 256 == 0
-    assert mf.retrieve_workspace_bytes(256, 16, 4, 64, __import__("torch").float32) == 0
+    # the retrieval kernels need no scratch: every configuration reports 0
+    import torch
+    for args in [(8192, 64, 8, 128, torch.bfloat16), (4096, 64, 8, 128, torch.float16),
+                 (256, 16, 4, 64, torch.float32)]:
+        assert mf.retrieve_workspace_bytes(*args) == 0
     assert L.mf_retrieve_workspace_bytes(0, 64, 8, 128, 2) == 0
 
 
@@ -130,8 +132,6 @@ def _retr(L, **kw):
     (dict(nnzb=-1), "nnzb"),
     (dict(vals=None), "null col_idx/vals"),
     (dict(dt=3), "dtype"),
-    (dict(ws=None), "workspace"),
-    (dict(ws_bytes=1000), "workspace"),
 ])
 def test_retrieve_rejects(L, kw, frag):
     assert _retr(L, **kw) == mf.MF_ERR_INVALID
