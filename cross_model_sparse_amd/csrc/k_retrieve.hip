@@ -57,6 +57,8 @@ using namespace mfd;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;          // MFMA kernel workgroup
@@ -94,8 +96,24 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
 }
+// A wave-uniform pointer, guaranteed to live in scalar registers.
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const void*>(((unsigned long long)hi << 32) | lo);
+}
+// Same copy with a wave-uniform base address and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(unsigned voff, const void* sbase, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
+}
+// 8-byte register loads: per-lane address, or wave-uniform base + 32-bit offset.
 __device__ __forceinline__ void gload8(u32x2& r, const void* g) {
   asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(g) : "memory");
+}
+__device__ __forceinline__ void gload8s(u32x2& r, unsigned voff, const void* sbase) {
+  asm volatile("global_load_dwordx2 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -262,14 +280,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   // tile-slice copy d of this wavefront: 1 KB piece pr = heads 2pr, 2pr+1;
   // lane -> (head 2pr + lane/32, tile row (lane%32)/2, 16-byte half lane%2)
   const int64_t lane_off = (int64_t)(sub * kRows + ((lane & 31) >> 1)) * B + (lane & 1) * 8;
-  int64_t head_off[NDV];
+  unsigned head_off[NDV];                        // byte offset of this lane's 16 bytes in a block
   int piece[NDV];
 #pragma unroll
   for (int d = 0; d < NDV; ++d) {
     const int pr = wave + kWaves * d < NPR ? wave + kWaves * d : NPR - 1;  // surplus copies repeat the last piece
     int s = 2 * pr + (lane >> 5);
     s = s < H_s ? s : H_s - 1;                  // padding slots get a real head (zero weight)
-    head_off[d] = s * tile + lane_off;
+    head_off[d] = (unsigned)((s * tile + lane_off) * 2);
     piece[d] = pr;
   }
   const unsigned smem_lds = lds_addr(smem);
@@ -278,19 +296,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const unsigned short* src = vals + block_of(x) * H_s * tile + (xc & ncc_mask) * kCB;
     const unsigned base = smem_lds + slot * kStage;
 #pragma unroll
-    for (int d = 0; d < NDV; ++d) dma16(src + head_off[d], base + piece[d] * 1024);
+    for (int d = 0; d < NDV; ++d) dma16s(head_off[d], src, base + piece[d] * 1024);
   };
   // V rows of chunk x: lane -> keys 8*(lane/32)..+7 of the chunk, head-dim
-  // columns 4*(lane%32)..+3 of KV head g (rows past N read row N-1, whose
-  // weight is zero)
+  // columns 4*(lane%32)..+3 of KV head g.  A chunk that reaches past row N
+  // (only the last one of a partial block) reads row N-1 instead, whose weight
+  // is zero.
   const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
+  const unsigned v_off = (unsigned)(((int64_t)8 * (lane >> 5) * ldV + g * kD + 4 * (lane & 31)) * 2);
   auto issue_v = [&](int x, int J, u32x2 (&vr)[8]) {
     const int xc = x < n_chunks ? x : n_chunks - 1;
-    const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB + 8 * (lane >> 5);
+    const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB;
+    if (key0 + kCB <= N) {
+      const unsigned short* rowp = V + (int64_t)key0 * ldV;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = key0 + j < N ? key0 + j : N - 1;
-      gload8(vr[j], vlane + (int64_t)key * ldV);
+      for (int j = 0; j < 8; ++j) gload8s(vr[j], v_off, rowp + j * ldV);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = key0 + 8 * (lane >> 5) + j;
+        gload8(vr[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
+      }
     }
   };
 
@@ -332,22 +358,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int r = 16 * hm_mt + 4 * q + a;
-      float v[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = c[t][a] * sc;
+      const f32x2 v01 = {c[0][a] * sc, c[1][a] * sc};
+      const f32x2 v23 = {c[2][a] * sc, c[3][a] * sc};
       if constexpr (kBF16) {
-        unsigned short hi[4], lo[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          hi[t] = bf16_bits(v[t]);
-          lo[t] = bf16_bits(v[t] - bf16_to_f32(hi[t]));
-        }
-        *reinterpret_cast<u32x2*>(dst + r * 512) =
-            u32x2{(unsigned)hi[0] | ((unsigned)hi[1] << 16), (unsigned)hi[2] | ((unsigned)hi[3] << 16)};
-        *reinterpret_cast<u32x2*>(dst + kPlane + r * 512) =
-            u32x2{(unsigned)lo[0] | ((unsigned)lo[1] << 16), (unsigned)lo[2] | ((unsigned)lo[3] << 16)};
+        const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector(v01, bf16x2));
+        const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector(v23, bf16x2));
+        const f32x2 r01 = {v01[0] - __uint_as_float(h01 << 16), v01[1] - __uint_as_float(h01 & 0xffff0000u)};
+        const f32x2 r23 = {v23[0] - __uint_as_float(h23 << 16), v23[1] - __uint_as_float(h23 & 0xffff0000u)};
+        const unsigned l01 = __builtin_bit_cast(unsigned, __builtin_convertvector(r01, bf16x2));
+        const unsigned l23 = __builtin_bit_cast(unsigned, __builtin_convertvector(r23, bf16x2));
+        *reinterpret_cast<u32x2*>(dst + r * 512) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(dst + kPlane + r * 512) = u32x2{l01, l23};
       } else {
-        *reinterpret_cast<u32x2*>(dst + r * 512) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(dst + r * 512) =
+            u32x2{pack_f16x2(v01[0], v01[1]), pack_f16x2(v23[0], v23[1])};
       }
     }
   };
@@ -376,8 +400,88 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     }
   };
 
+  // One phase's compute, in an explicit order that keeps the matrix cores fed:
+  // head-mix operand reads, head-mix MFMAs with the next operand's transpose
+  // between them, then the A.V MFMAs with the packing of the head-mix result
+  // between them.  sched_barrier stops the compiler from regrouping the parts.
+  auto compute = [&](int slot, bool keep, int ab_hm, int ab_av, const u32x2 (&vr)[8]) {
+    const unsigned char* st = smem + slot * kStage + hrow * 32 + hkq * 8;
+    f32x4 c[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x2 x[8];
+    {
+      const int ch = Plan::chunk(0, q) < 0 ? 0 : Plan::chunk(0, q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x2*>(st + (8 * ch + j) * kHeadSlot);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NBOP; ++b) {
+      u32x4 y[4];
+      transpose8x4(x, y);
+      if (b + 1 < NBOP) {
+        const int ch = Plan::chunk(b + 1, q) < 0 ? 0 : Plan::chunk(b + 1, q);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x2*>(st + (8 * ch + j) * kHeadSlot);
+      }
+#pragma unroll
+      for (int w = 0; w < Plan::nw(b); ++w)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (kBF16)
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wop[b][w]), as_bf16x8(y[t]), c[t], 0, 0, 0);
+          else
+            c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wop[b][w]), as_f16x8(y[t]), c[t], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // A.V operands
+    u32x4 vt[4];
+    transpose8x4(vr, vt);
+    const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
+    const float sc = keep ? 1.f : 0.f;
+    unsigned char* dst = smem + kAhatOff + ab_hm * kAhatBuf + hm_off;
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      const int r = rbeg + 2 * p + (am >> 4);
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        const u32x4 a4 = *reinterpret_cast<const u32x4*>(asrc + pl * kPlane + r * 512);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          if constexpr (kBF16)
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a4), as_bf16x8(vt[dt]), acc[p][dt], 0, 0, 0);
+          else
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a4), as_f16x8(vt[dt]), acc[p][dt], 0, 0, 0);
+        }
+        // pack receiver row a = 2p + pl of the head-mix result between the MFMAs
+        constexpr int kSteps = NPAIR * NPL;
+#pragma unroll
+        for (int a = (p * NPL + pl) * 4 / kSteps; a < (p * NPL + pl + 1) * 4 / kSteps; ++a) {
+          const int rr = 16 * hm_mt + 4 * q + a;
+          const f32x2 v01 = {c[0][a] * sc, c[1][a] * sc};
+          const f32x2 v23 = {c[2][a] * sc, c[3][a] * sc};
+          if constexpr (kBF16) {
+            const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector(v01, bf16x2));
+            const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector(v23, bf16x2));
+            const f32x2 r01 = {v01[0] - __uint_as_float(h01 << 16), v01[1] - __uint_as_float(h01 & 0xffff0000u)};
+            const f32x2 r23 = {v23[0] - __uint_as_float(h23 << 16), v23[1] - __uint_as_float(h23 & 0xffff0000u)};
+            const unsigned l01 = __builtin_bit_cast(unsigned, __builtin_convertvector(r01, bf16x2));
+            const unsigned l23 = __builtin_bit_cast(unsigned, __builtin_convertvector(r23, bf16x2));
+            *reinterpret_cast<u32x2*>(dst + rr * 512) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2*>(dst + kPlane + rr * 512) = u32x2{l01, l23};
+          } else {
+            *reinterpret_cast<u32x2*>(dst + rr * 512) =
+                u32x2{pack_f16x2(v01[0], v01[1]), pack_f16x2(v23[0], v23[1])};
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // ---- pipeline ---------------------------------------------------------------
-  // phase u: issue V(u+1) and tile slice u+3, A.V(u), head mix(u+1), wait, barrier
   u32x2 vA[8], vB[8];
   int J1 = 0;                                    // column of chunk u+1
   if (n_chunks > 0) {
@@ -399,9 +503,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const int Jn = col_idx[block_of(u + 2)];
     issue_v(u + 1, J1, vnext);
     issue_vals(u + 3, slot);
-    a_dot_v(u & 1, vcur);
     const int s1 = slot == 2 ? 0 : slot + 1;
-    head_mix(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1);
+    const bool keep1 = u + 1 < n_chunks && col_ok(J1);
+    compute(s1, keep1, (u + 1) & 1, u & 1, vcur);
     wait_vm_tied<NDV>(vnext);                    // V(u+1) and slice u+2 landed
     lds_barrier();
     J1 = Jn;
@@ -572,7 +676,8 @@ bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const 
   if (H_r % 8 != 0 || H_r > kMaxRecv) return false;
   const int G = H_r / H_kv, RPW = H_r / 8;
   if (G % RPW != 0) return false;
-  return aligned(vals, 16) && aligned(O, 16) && ldO % 8 == 0 && aligned(V, 8) && ldV % 4 == 0;
+  return aligned(vals, 16) && aligned(O, 16) && ldO % 8 == 0 && aligned(V, 8) && ldV % 4 == 0 &&
+         ldV <= (int64_t)1 << 26;   // per-lane V offsets are 32-bit
 }
 
 size_t retrieve_workspace_bytes(int, int, int, int, int) { return 0; }
