@@ -91,9 +91,13 @@ __device__ __forceinline__ void transpose8x4(const u32x2 (&x)[8], u32x4 (&y)[4])
 // and waits on it explicitly.  Loads return in issue order, so "at most n
 // newer operations outstanding" identifies exactly which data has landed; the
 // compiler, unaware of these operations, adds no conservative waits of its own.
+// Hazards the compiler does not see through inline asm, handled inside each
+// statement: an SGPR written by a VALU instruction (v_readfirstlane) needs 5
+// wait states before a vector-memory instruction reads it (s_nop 4), and M0
+// written by SALU needs 1 before an LDS DMA reads it (s_nop 0).
 __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
   // 16 bytes per lane from memory straight into LDS at lds_base + 16 * lane
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
 }
 // A wave-uniform pointer, guaranteed to live in scalar registers.
@@ -105,15 +109,30 @@ __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
 }
 // Same copy with a wave-uniform base address and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16s(unsigned voff, const void* sbase, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
 }
-// 8-byte register loads: per-lane address, or wave-uniform base + 32-bit offset.
+// 8-byte register loads: per-lane address ...
 __device__ __forceinline__ void gload8(u32x2& r, const void* g) {
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(g) : "memory");
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(r) : "v"(g) : "memory");
 }
-__device__ __forceinline__ void gload8s(u32x2& r, unsigned voff, const void* sbase) {
-  asm volatile("global_load_dwordx2 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
+// ... or eight rows at once: wave-uniform row bases + one 32-bit per-lane offset
+__device__ __forceinline__ void gload8x8s(u32x2 (&r)[8], unsigned voff, const void* const (&b)[8]) {
+  asm volatile("s_nop 4\n\t"
+               "global_load_dwordx2 %0, %8, %9\n\t"
+               "global_load_dwordx2 %1, %8, %10\n\t"
+               "global_load_dwordx2 %2, %8, %11\n\t"
+               "global_load_dwordx2 %3, %8, %12\n\t"
+               "global_load_dwordx2 %4, %8, %13\n\t"
+               "global_load_dwordx2 %5, %8, %14\n\t"
+               "global_load_dwordx2 %6, %8, %15\n\t"
+               "global_load_dwordx2 %7, %8, %16"
+               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+                 "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+               : "v"(voff), "s"(sgpr_ptr(b[0])), "s"(sgpr_ptr(b[1])), "s"(sgpr_ptr(b[2])),
+                 "s"(sgpr_ptr(b[3])), "s"(sgpr_ptr(b[4])), "s"(sgpr_ptr(b[5])),
+                 "s"(sgpr_ptr(b[6])), "s"(sgpr_ptr(b[7]))
+               : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -309,8 +328,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB;
     if (key0 + kCB <= N) {
       const unsigned short* rowp = V + (int64_t)key0 * ldV;
+      const void* rows[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) gload8s(vr[j], v_off, rowp + j * ldV);
+      for (int j = 0; j < 8; ++j) rows[j] = rowp + j * ldV;
+      gload8x8s(vr, v_off, rows);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -482,38 +503,86 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   };
 
   // ---- pipeline ---------------------------------------------------------------
-  u32x2 vA[8], vB[8];
-  int J1 = 0;                                    // column of chunk u+1
-  if (n_chunks > 0) {
-    const int J0 = col_idx[block_of(0)];
-    J1 = col_idx[block_of(1)];
-    issue_v(0, J0, vA);
-    issue_vals(0, 0);
-    issue_vals(1, 1);
-    issue_vals(2, 2);
-    wait_vm_tied<2 * NDV>(vA);                   // V(0) and slice 0 landed
-    lds_barrier();
-    head_mix(0, col_ok(J0), 0);
-    wait_vm<NDV>();                              // slice 1 landed
-    lds_barrier();
-  }
-  const int n_pad = (n_chunks + 1) & ~1;
+  // Phase u: load V(u+2) and copy tile slice u+3 (in the order the data is
+  // needed), head mix(u+1) and A.V(u) (compute), wait for slice u+2 and V(u+1),
+  // barrier.  V lives in three register sets, so the loop is unrolled by three
+  // and the chunk count padded with empty chunks (zero mixed map).  Where three
+  // sets do not fit the register budget (bf16, 41..48 sender heads) V(u+1) is
+  // loaded in phase u instead, from two sets.
+  constexpr int NVS = (kBF16 && NCH == 6) ? 2 : 3;
+  u32x2 vA[8], vB[8], vC[8];
+  int J1 = 0, J2 = 0;                            // columns of chunks u+1, u+2
   int slot = 0;                                  // u % 3
-  auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8]) {
-    const int Jn = col_idx[block_of(u + 2)];
-    issue_v(u + 1, J1, vnext);
-    issue_vals(u + 3, slot);
-    const int s1 = slot == 2 ? 0 : slot + 1;
-    const bool keep1 = u + 1 < n_chunks && col_ok(J1);
-    compute(s1, keep1, (u + 1) & 1, u & 1, vcur);
-    wait_vm_tied<NDV>(vnext);                    // V(u+1) and slice u+2 landed
-    lds_barrier();
-    J1 = Jn;
-    slot = s1;
-  };
-  for (int u = 0; u < n_pad; u += 2) {
-    phase(u, vA, vB);
-    phase(u + 1, vB, vA);
+  if constexpr (NVS == 3) {
+    if (n_chunks > 0) {
+      const int J0 = col_idx[block_of(0)];
+      J1 = col_idx[block_of(1)];
+      J2 = col_idx[block_of(2)];
+      issue_vals(0, 0);
+      issue_vals(1, 1);
+      issue_v(0, J0, vA);
+      issue_vals(2, 2);
+      issue_v(1, J1, vB);
+      wait_vm<2 * (NDV + 8)>();                  // slice 0 landed
+      lds_barrier();
+      head_mix(0, col_ok(J0), 0);
+      wait_vm_tied<NDV + 8>(vA);                 // slice 1 and V(0) landed
+      lds_barrier();
+    }
+    const int n_pad = (n_chunks + 2) / 3 * 3;
+    auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8], u32x2 (&vfree)[8]) {
+      const int Jn = col_idx[block_of(u + 3)];
+      issue_vals(u + 3, slot);
+      issue_v(u + 2, J2, vfree);
+      const int s1 = slot == 2 ? 0 : slot + 1;
+      compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vcur);
+      wait_vm_tied<NDV + 8>(vnext);              // slice u+2 and V(u+1) landed
+      lds_barrier();
+      J1 = J2;
+      J2 = Jn;
+      slot = s1;
+    };
+    for (int u = 0; u < n_pad; u += 3) {
+      phase(u, vA, vB, vC);
+      phase(u + 1, vB, vC, vA);
+      phase(u + 2, vC, vA, vB);
+    }
+    // every V register set is retired (tied) before its registers can be reused
+    wait_vm_tied<0>(vA);
+    wait_vm_tied<0>(vB);
+    wait_vm_tied<0>(vC);
+  } else {
+    if (n_chunks > 0) {
+      const int J0 = col_idx[block_of(0)];
+      J1 = col_idx[block_of(1)];
+      issue_v(0, J0, vA);
+      issue_vals(0, 0);
+      issue_vals(1, 1);
+      issue_vals(2, 2);
+      wait_vm_tied<2 * NDV>(vA);                 // V(0) and slice 0 landed
+      lds_barrier();
+      head_mix(0, col_ok(J0), 0);
+      wait_vm<NDV>();                            // slice 1 landed
+      lds_barrier();
+    }
+    const int n_pad = (n_chunks + 1) & ~1;
+    auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8]) {
+      const int Jn = col_idx[block_of(u + 2)];
+      issue_v(u + 1, J1, vnext);
+      issue_vals(u + 3, slot);
+      const int s1 = slot == 2 ? 0 : slot + 1;
+      compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vcur);
+      wait_vm_tied<NDV>(vnext);                  // V(u+1) and slice u+2 landed
+      lds_barrier();
+      J1 = Jn;
+      slot = s1;
+    };
+    for (int u = 0; u < n_pad; u += 2) {
+      phase(u, vA, vB);
+      phase(u + 1, vB, vA);
+    }
+    wait_vm_tied<0>(vA);
+    wait_vm_tied<0>(vB);
   }
   wait_vm<0>();
   lds_barrier();
