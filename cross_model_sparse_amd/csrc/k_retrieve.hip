@@ -71,6 +71,7 @@ constexpr int kMaxHs = 48;                     // sender heads of the MFMA kerne
 constexpr int kHeadSlot = kRows * kCB * 2;     // bytes: one head of one tile slice
 constexpr int kPlane = kMaxRecv * kRows * kCB * 2;  // bytes: one mixed-map plane
 constexpr int kOutSlot = 2 * kRows * kD * 2;   // bytes: a receiver pair's output rows
+constexpr int kVSlot = kCB * kD * 2;           // bytes: one KV head's V rows of one chunk
 
 __device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -112,42 +113,10 @@ __device__ __forceinline__ void dma16s(unsigned voff, const void* sbase, unsigne
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
 }
-// 8-byte register loads: per-lane address ...
-__device__ __forceinline__ void gload8(u32x2& r, const void* g) {
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(r) : "v"(g) : "memory");
-}
-// ... or eight rows at once: wave-uniform row bases + one 32-bit per-lane offset
-__device__ __forceinline__ void gload8x8s(u32x2 (&r)[8], unsigned voff, const void* const (&b)[8]) {
-  asm volatile("s_nop 4\n\t"
-               "global_load_dwordx2 %0, %8, %9\n\t"
-               "global_load_dwordx2 %1, %8, %10\n\t"
-               "global_load_dwordx2 %2, %8, %11\n\t"
-               "global_load_dwordx2 %3, %8, %12\n\t"
-               "global_load_dwordx2 %4, %8, %13\n\t"
-               "global_load_dwordx2 %5, %8, %14\n\t"
-               "global_load_dwordx2 %6, %8, %15\n\t"
-               "global_load_dwordx2 %7, %8, %16"
-               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
-                 "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-               : "v"(voff), "s"(sgpr_ptr(b[0])), "s"(sgpr_ptr(b[1])), "s"(sgpr_ptr(b[2])),
-                 "s"(sgpr_ptr(b[3])), "s"(sgpr_ptr(b[4])), "s"(sgpr_ptr(b[5])),
-                 "s"(sgpr_ptr(b[6])), "s"(sgpr_ptr(b[7]))
-               : "memory");
-}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-// Same wait; the registers of an asm load are tied to it, so no use of them
-// can be scheduled before the data has arrived.
-template <int N>
-__device__ __forceinline__ void wait_vm_tied(u32x2 (&r)[8]) {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]),
-                 "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7])
-               : "n"(N) : "memory");
 }
 // Workgroup barrier for LDS traffic only (outstanding memory loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
@@ -221,13 +190,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   using Plan = HmPlan<kBF16, NCH>;
   constexpr int NBOP = Plan::NBOP;
   constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
-  constexpr int NSTG = 3;                          // tile-slice buffers
+  constexpr int NSTG = (kBF16 && NCH == 6) ? 2 : 3;  // tile-slice buffers (LDS budget)
   constexpr int kStage = 8 * NCH * kHeadSlot;      // one tile slice: head slots 0..8*NCH-1
   constexpr int NPR = 4 * NCH;                     // 1 KB copies per tile slice
   constexpr int NDV = (NPR + kWaves - 1) / kWaves; // copies per wavefront per slice
   constexpr int kAhatOff = NSTG * kStage;
   constexpr int kAhatBuf = NPL * kPlane;
-  constexpr int kUsed = kAhatOff + 2 * kAhatBuf;
+  constexpr int kVOff = kAhatOff + 2 * kAhatBuf;   // per-wavefront V slots
+  constexpr int kUsed = kVOff + kWaves * kVSlot;
   constexpr int kSmem = kUsed > kWaves * kOutSlot ? kUsed : kWaves * kOutSlot;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   static_assert(NPAIR == 1 || NPAIR == 2, "receiver pairs per wavefront");
@@ -296,49 +266,75 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   };
   auto col_ok = [&](int J) { return J >= 0 && J < T; };
 
-  // tile-slice copy d of this wavefront: 1 KB piece pr = heads 2pr, 2pr+1;
+  // tile-slice copy d of this wavefront: 1 KB piece pr = wave + 8d (heads 2pr,
+  // 2pr+1), issued only for pr < NPR, so wavefronts issue NDV or NDV-1 copies;
   // lane -> (head 2pr + lane/32, tile row (lane%32)/2, 16-byte half lane%2)
+  const int ndv_w = (NPR - wave + kWaves - 1) / kWaves;  // copies of this wavefront
   const int64_t lane_off = (int64_t)(sub * kRows + ((lane & 31) >> 1)) * B + (lane & 1) * 8;
   unsigned head_off[NDV];                        // byte offset of this lane's 16 bytes in a block
-  int piece[NDV];
 #pragma unroll
   for (int d = 0; d < NDV; ++d) {
-    const int pr = wave + kWaves * d < NPR ? wave + kWaves * d : NPR - 1;  // surplus copies repeat the last piece
-    int s = 2 * pr + (lane >> 5);
+    int s = 2 * (wave + kWaves * d) + (lane >> 5);
     s = s < H_s ? s : H_s - 1;                  // padding slots get a real head (zero weight)
     head_off[d] = (unsigned)((s * tile + lane_off) * 2);
-    piece[d] = pr;
   }
   const unsigned smem_lds = lds_addr(smem);
-  auto issue_vals = [&](int x, int slot) {
+  auto vals_src = [&](int x) -> const unsigned short* {
     const int xc = x < n_chunks ? x : n_chunks - 1;
-    const unsigned short* src = vals + block_of(x) * H_s * tile + (xc & ncc_mask) * kCB;
-    const unsigned base = smem_lds + slot * kStage;
-#pragma unroll
-    for (int d = 0; d < NDV; ++d) dma16s(head_off[d], src, base + piece[d] * 1024);
+    return vals + block_of(x) * H_s * tile + (xc & ncc_mask) * kCB;
   };
-  // V rows of chunk x: lane -> keys 8*(lane/32)..+7 of the chunk, head-dim
-  // columns 4*(lane%32)..+3 of KV head g.  A chunk that reaches past row N
-  // (only the last one of a partial block) reads row N-1 instead, whose weight
-  // is zero.
-  const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
-  const unsigned v_off = (unsigned)(((int64_t)8 * (lane >> 5) * ldV + g * kD + 4 * (lane & 31)) * 2);
-  auto issue_v = [&](int x, int J, u32x2 (&vr)[8]) {
+  auto copy_piece = [&](const unsigned short* src, int slot, int d) {
+    if (d < ndv_w) dma16s(head_off[d], src, smem_lds + slot * kStage + (wave + kWaves * d) * 1024);
+  };
+  auto issue_vals = [&](int x, int slot) {
+    const unsigned short* src = vals_src(x);
+#pragma unroll
+    for (int d = 0; d < NDV; ++d) copy_piece(src, slot, d);
+  };
+  // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 2 NDV]
+  auto wait_vm_n = [&](int n) {
+    switch (n) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<1>(); break;
+      case 2: wait_vm<2>(); break;
+      case 3: wait_vm<3>(); break;
+      case 4: wait_vm<4>(); break;
+      case 5: wait_vm<5>(); break;
+      default: wait_vm<6>(); break;
+    }
+  };
+  static_assert(NDV <= 3, "copies per wavefront per slice");
+
+  // V rows of chunk x for this wavefront's KV head g: 16 keys x 128 columns,
+  // copied as four 1 KB pieces (lane -> key 4m + lane/16, columns
+  // 8*(lane%16)..+7) into the wavefront's own LDS slot [16 keys][128].  A chunk
+  // that reaches past row N (only the last one of a partial block) copies row
+  // N-1 instead, whose weight is zero.
+  const unsigned vslot = smem_lds + kVOff + wave * kVSlot;
+  const unsigned v_off = (unsigned)(((int64_t)(lane >> 4) * ldV + g * kD + (lane & 15) * 8) * 2);
+  const unsigned short* vlane = V + (int64_t)g * kD + (lane & 15) * 8;
+  auto issue_v = [&](int x, int J) {
     const int xc = x < n_chunks ? x : n_chunks - 1;
     const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB;
     if (key0 + kCB <= N) {
-      const unsigned short* rowp = V + (int64_t)key0 * ldV;
-      const void* rows[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rows[j] = rowp + j * ldV;
-      gload8x8s(vr, v_off, rows);
+      for (int m = 0; m < 4; ++m) dma16s(v_off, V + (int64_t)(key0 + 4 * m) * ldV, vslot + m * 1024);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = key0 + 8 * (lane >> 5) + j;
-        gload8(vr[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
+      for (int m = 0; m < 4; ++m) {
+        const int key = key0 + 4 * m + (lane >> 4);
+        dma16(vlane + (int64_t)(key < N ? key : N - 1) * ldV, vslot + m * 1024);
       }
     }
+  };
+  // A.V B operand from the slot: lane -> keys 8*(lane/32)..+7, columns
+  // 4*(lane%32)..+3, transposed to vt[dt] = 8 keys of column 4*(lane%32)+dt
+  const unsigned char* vsl = smem + kVOff + wave * kVSlot + 8 * (lane & 31) + 2048 * (lane >> 5);
+  auto read_vt = [&](u32x4 (&vt)[4]) {
+    u32x2 xv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xv[j] = *reinterpret_cast<const u32x2*>(vsl + j * 256);
+    transpose8x4(xv, vt);
   };
 
   // head mix of chunk x from tile slot `slot` into mixed-map buffer `ab`;
@@ -397,35 +393,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     }
   };
 
-  // A.V of the chunk whose mixed map is in buffer `ab` and V rows in `vr`
+  // A.V operand addressing
   const int am = lane & 31;
   const int a_off = (am & 15) * 32 + (((lane >> 5) ^ ((am >> 2) & 1)) * 16);
-  auto a_dot_v = [&](int ab, const u32x2 (&vr)[8]) {
-    u32x4 vt[4];                                 // vt[dt]: 8 keys of column 4*(lane%32)+dt
-    transpose8x4(vr, vt);
-    const unsigned char* src = smem + kAhatOff + ab * kAhatBuf + a_off;
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p) {
-      const int r = rbeg + 2 * p + (am >> 4);
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) {
-        const u32x4 a4 = *reinterpret_cast<const u32x4*>(src + pl * kPlane + r * 512);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          if constexpr (kBF16)
-            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a4), as_bf16x8(vt[dt]), acc[p][dt], 0, 0, 0);
-          else
-            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a4), as_f16x8(vt[dt]), acc[p][dt], 0, 0, 0);
-        }
-      }
-    }
-  };
 
   // One phase's compute, in an explicit order that keeps the matrix cores fed:
   // head-mix operand reads, head-mix MFMAs with the next operand's transpose
   // between them, then the A.V MFMAs with the packing of the head-mix result
   // between them.  sched_barrier stops the compiler from regrouping the parts.
-  auto compute = [&](int slot, bool keep, int ab_hm, int ab_av, const u32x2 (&vr)[8]) {
+  auto compute = [&](int slot, bool keep, int ab_hm, int ab_av, const u32x4 (&vt)[4], auto&& mid_copy, auto&& step_copy) {
     const unsigned char* st = smem + slot * kStage + hrow * 32 + hkq * 8;
     f32x4 c[4];
 #pragma unroll
@@ -436,6 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x2*>(st + (8 * ch + j) * kHeadSlot);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mid_copy();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < NBOP; ++b) {
@@ -458,8 +436,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
       __builtin_amdgcn_sched_barrier(0);
     }
     // A.V operands
-    u32x4 vt[4];
-    transpose8x4(vr, vt);
     const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
     const float sc = keep ? 1.f : 0.f;
     unsigned char* dst = smem + kAhatOff + ab_hm * kAhatBuf + hm_off;
@@ -497,92 +473,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
                 u32x2{pack_f16x2(v01[0], v01[1]), pack_f16x2(v23[0], v23[1])};
           }
         }
+        step_copy(p * NPL + pl);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
   // ---- pipeline ---------------------------------------------------------------
-  // Phase u: load V(u+2) and copy tile slice u+3 (in the order the data is
-  // needed), head mix(u+1) and A.V(u) (compute), wait for slice u+2 and V(u+1),
-  // barrier.  V lives in three register sets, so the loop is unrolled by three
-  // and the chunk count padded with empty chunks (zero mixed map).  Where three
-  // sets do not fit the register budget (bf16, 41..48 sender heads) V(u+1) is
-  // loaded in phase u instead, from two sets.
-  constexpr int NVS = (kBF16 && NCH == 6) ? 2 : 3;
-  u32x2 vA[8], vB[8], vC[8];
-  int J1 = 0, J2 = 0;                            // columns of chunks u+1, u+2
-  int slot = 0;                                  // u % 3
-  if constexpr (NVS == 3) {
-    if (n_chunks > 0) {
-      const int J0 = col_idx[block_of(0)];
-      J1 = col_idx[block_of(1)];
-      J2 = col_idx[block_of(2)];
-      issue_vals(0, 0);
-      issue_vals(1, 1);
-      issue_v(0, J0, vA);
-      issue_vals(2, 2);
-      issue_v(1, J1, vB);
-      wait_vm<2 * (NDV + 8)>();                  // slice 0 landed
-      lds_barrier();
-      head_mix(0, col_ok(J0), 0);
-      wait_vm_tied<NDV + 8>(vA);                 // slice 1 and V(0) landed
-      lds_barrier();
-    }
-    const int n_pad = (n_chunks + 2) / 3 * 3;
-    auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8], u32x2 (&vfree)[8]) {
-      const int Jn = col_idx[block_of(u + 3)];
-      issue_vals(u + 3, slot);
-      issue_v(u + 2, J2, vfree);
-      const int s1 = slot == 2 ? 0 : slot + 1;
-      compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vcur);
-      wait_vm_tied<NDV + 8>(vnext);              // slice u+2 and V(u+1) landed
-      lds_barrier();
-      J1 = J2;
-      J2 = Jn;
-      slot = s1;
+  // Phase u: V(u) from the wavefront's slot into registers; head-mix operand
+  // reads; copy V(u+1) into the (now read) slot; head mix(u+1); A.V(u) with the
+  // copies of tile slice u+NSTG issued between its MFMAs, so that the copies
+  // drain through the vector-memory path while the matrix cores work; wait for
+  // V(u+1) and slice u+2; barrier.  Each wavefront copies and reads only its own
+  // V slot; tile slices are shared through the barrier.
+  constexpr int kSteps = NPAIR * NPL;            // A.V steps that can carry a copy
+  int J1 = 0;                                    // column of chunk u+1
+  int slot = 0;                                  // u % NSTG
+  if (n_chunks > 0) {
+    const int J0 = col_idx[block_of(0)];
+    J1 = col_idx[block_of(1)];
+    issue_v(0, J0);
+#pragma unroll
+    for (int st = 0; st < NSTG; ++st) issue_vals(st, st);
+    wait_vm_n((NSTG - 1) * ndv_w);               // V(0) and slice 0 landed
+    lds_barrier();
+    head_mix(0, col_ok(J0), 0);
+    wait_vm_n((NSTG - 2) * ndv_w);               // slice 1 landed
+    lds_barrier();
+  }
+  for (int u = 0; u < n_chunks; ++u) {
+    const int Jn = col_idx[block_of(u + 2)];
+    u32x4 vt[4];
+    read_vt(vt);
+    const unsigned short* vsrc = vals_src(u + NSTG);
+    const int cur = slot;
+    const int s1 = slot + 1 == NSTG ? 0 : slot + 1;
+    auto mid_copy = [&]() {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot read before it is refilled
+      issue_v(u + 1, J1);
     };
-    for (int u = 0; u < n_pad; u += 3) {
-      phase(u, vA, vB, vC);
-      phase(u + 1, vB, vC, vA);
-      phase(u + 2, vC, vA, vB);
-    }
-    // every V register set is retired (tied) before its registers can be reused
-    wait_vm_tied<0>(vA);
-    wait_vm_tied<0>(vB);
-    wait_vm_tied<0>(vC);
-  } else {
-    if (n_chunks > 0) {
-      const int J0 = col_idx[block_of(0)];
-      J1 = col_idx[block_of(1)];
-      issue_v(0, J0, vA);
-      issue_vals(0, 0);
-      issue_vals(1, 1);
-      issue_vals(2, 2);
-      wait_vm_tied<2 * NDV>(vA);                 // V(0) and slice 0 landed
-      lds_barrier();
-      head_mix(0, col_ok(J0), 0);
-      wait_vm<NDV>();                            // slice 1 landed
-      lds_barrier();
-    }
-    const int n_pad = (n_chunks + 1) & ~1;
-    auto phase = [&](int u, u32x2 (&vcur)[8], u32x2 (&vnext)[8]) {
-      const int Jn = col_idx[block_of(u + 2)];
-      issue_v(u + 1, J1, vnext);
-      issue_vals(u + 3, slot);
-      const int s1 = slot == 2 ? 0 : slot + 1;
-      compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vcur);
-      wait_vm_tied<NDV>(vnext);                  // V(u+1) and slice u+2 landed
-      lds_barrier();
-      J1 = Jn;
-      slot = s1;
+    auto step_copy = [&](int step) {
+      // tile-slice copies spread over the A.V steps; the last step takes the rest
+#pragma unroll
+      for (int d = 0; d < NDV; ++d)
+        if ((d * kSteps) / NDV == step || (step == kSteps - 1 && (d * kSteps) / NDV >= kSteps))
+          copy_piece(vsrc, cur, d);
     };
-    for (int u = 0; u < n_pad; u += 2) {
-      phase(u, vA, vB);
-      phase(u + 1, vB, vA);
-    }
-    wait_vm_tied<0>(vA);
-    wait_vm_tied<0>(vB);
+    compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vt, mid_copy, step_copy);
+    wait_vm_n((NSTG - 2) * ndv_w);               // V(u+1) and slice u+2 landed
+    lds_barrier();
+    J1 = Jn;
+    slot = s1;
   }
   wait_vm<0>();
   lds_barrier();
@@ -745,7 +686,7 @@ bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const 
   if (H_r % 8 != 0 || H_r > kMaxRecv) return false;
   const int G = H_r / H_kv, RPW = H_r / 8;
   if (G % RPW != 0) return false;
-  return aligned(vals, 16) && aligned(O, 16) && ldO % 8 == 0 && aligned(V, 8) && ldV % 4 == 0 &&
+  return aligned(vals, 16) && aligned(O, 16) && ldO % 8 == 0 && aligned(V, 16) && ldV % 8 == 0 &&
          ldV <= (int64_t)1 << 26;   // per-lane V offsets are 32-bit
 }
 
