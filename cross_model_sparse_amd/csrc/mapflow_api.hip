@@ -139,6 +139,28 @@ size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype) {
   return mf::retrieve_workspace_bytes(N, B, H_kv, d, dtype);
 }
 
+// Shape and stride checks shared by mf_retrieve_fused and mf_retrieve_kernel.
+static int check_retrieve_shape(const char* fn, int dtype, int H_s, int N, int B, int H_r,
+                                int H_kv, int d, int64_t ldV, int64_t ldO) {
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (H_r < 1 || H_r > 64) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": H_r must be in [1, 64] (got %lld)", H_r));
+  if (H_kv < 1 || H_r % H_kv != 0)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": H_r = %lld is not a multiple of H_kv = %lld", H_r, H_kv));
+  if (d != 64 && d != 128) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": d must be 64 or 128 (got %lld)", d));
+  if (ldV < (int64_t)H_kv * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldV < H_kv*d");
+  if (ldO < (int64_t)H_r * d) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": ldO < H_r*d");
+  return MF_OK;
+}
+
+int mf_retrieve_kernel(int dtype, int H_s, int N, int B, int H_r, int H_kv, int d,
+                       const void* vals, const void* V, int64_t ldV, const void* O,
+                       int64_t ldO) {
+  const int st = check_retrieve_shape("mf_retrieve_kernel", dtype, H_s, N, B, H_r, H_kv, d, ldV, ldO);
+  if (st != MF_OK) return -st;
+  return mf::retrieve_uses_mfma(dtype, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO) ? 1 : 0;
+}
+
 int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                       const void* vals, int64_t nnzb, int dtype, int H_s,
                       int N, int B, const float* W, int H_r, const void* V,

@@ -34,6 +34,9 @@ int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
                     size_t workspace_bytes, hipStream_t st);
 size_t retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dt);
+// True when launch_retrieve runs the matrix-core kernel for these arguments.
+bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const void* vals,
+                        const void* V, int64_t ldV, const void* O, int64_t ldO);
 
 }  // namespace mf
 

@@ -24,7 +24,7 @@ _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_
 
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_retrieve_workspace_bytes",
-            "mf_retrieve_fused")
+            "mf_retrieve_kernel", "mf_retrieve_fused")
 
 
 class MapflowError(RuntimeError):
@@ -74,6 +74,9 @@ def load() -> ctypes.CDLL:
                                      c_sz, c_vp]
     L.mf_retrieve_workspace_bytes.restype = c_sz
     L.mf_retrieve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    L.mf_retrieve_kernel.restype = c_int
+    L.mf_retrieve_kernel.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
+                                     c_vp, c_i64, c_vp, c_i64]
     L.mf_retrieve_fused.restype = c_int
     L.mf_retrieve_fused.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
                                     c_vp, c_int, c_vp, c_int, c_int, c_i64, c_vp, c_i64,
@@ -178,6 +181,22 @@ def topp_select_bsr(mass: torch.Tensor, A: torch.Tensor, B: int, p: float,
     _check(st, int(n.value))
     nnzb = int(n.value) if sync else None
     return row_ptr, col_idx, vals, nnzb
+
+
+def retrieve_kernel(vals: torch.Tensor, V: torch.Tensor, W: torch.Tensor, N: int, B: int,
+                    out: torch.Tensor | None = None) -> str:
+    """'mfma' or 'plain': the kernel retrieve_fused runs for these tensors
+    (mf_retrieve_kernel; host-side decision, no GPU work)."""
+    H_s, H_r, H_kv, d = vals.shape[1], W.shape[0], V.shape[1], V.shape[2]
+    if out is None:
+        o_ptr, ldO = 256, H_r * d           # a fresh allocation is 256-byte aligned
+    else:
+        o_ptr, ldO = out.data_ptr(), out.stride(0)
+    r = load().mf_retrieve_kernel(_DTYPE_CODE[V.dtype], H_s, N, B, H_r, H_kv, d,
+                                  vals.data_ptr(), V.data_ptr(), V.stride(0), o_ptr, ldO)
+    if r < 0:
+        _check(-r)
+    return "mfma" if r == 1 else "plain"
 
 
 def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,

@@ -135,6 +135,20 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
 size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
 
 /*
+ * Which retrieval kernel mf_retrieve_fused runs for these arguments (host
+ * only, no GPU work; the three pointers are inspected for alignment only and
+ * may be any address with the alignment the real buffers will have).
+ *  Returns 1 for the matrix-core kernel (MF_F16/MF_BF16, d = 128, B in
+ *  {16,32,64,128}, H_s <= 48, H_r in {8,16,24,32} with each group of H_r/8
+ *  consecutive receiver heads inside one KV head, vals and O 16-byte aligned,
+ *  ldO % 8 == 0, V 16-byte aligned with ldV % 8 == 0), 0 for the plain kernel,
+ *  and -MF_ERR_INVALID when mf_retrieve_fused would reject the shapes.
+ */
+int mf_retrieve_kernel(int dtype, int H_s, int N, int B, int H_r, int H_kv, int d,
+                       const void* vals, const void* V, int64_t ldV, const void* O,
+                       int64_t ldO);
+
+/*
  * Fused head-mapped BSR retrieval (paper page, "MapFlow System Design" item 3,
  * highlights 2 and 4; article, second section and third component).
  *

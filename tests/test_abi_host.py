@@ -138,6 +138,45 @@ def test_retrieve_rejects(L, kw, frag):
     assert frag in _last(L)
 
 
+A16 = 0x100000                           # 16-byte aligned fake address
+
+
+@pytest.mark.parametrize("shape,expect", [
+    # (dtype, H_s, N, B, H_r, H_kv, d), kernel
+    ((2, 40, 8192, 64, 32, 8, 128), 1),      # 14B->8B-like pair, bf16
+    ((1, 32, 4096, 64, 24, 8, 128), 1),      # 8B->3B-like pair, fp16, G = 3
+    ((1, 32, 32768, 128, 32, 8, 128), 1),    # long context, B = 128
+    ((2, 32, 4096, 64, 24, 8, 128), 1),      # varlen pair, bf16
+    ((2, 16, 300, 32, 8, 2, 128), 1),        # one receiver per wavefront
+    ((2, 48, 520, 64, 32, 4, 128), 1),       # 48 sender heads (two tile buffers)
+    ((1, 8, 200, 16, 16, 8, 128), 1),        # B = 16
+    ((0, 4, 256, 16, 4, 4, 64), 0),          # fp32
+    ((1, 32, 400, 64, 24, 8, 64), 0),        # d = 64
+    ((2, 64, 520, 64, 32, 4, 128), 0),       # H_s > 48
+    ((2, 40, 260, 64, 48, 8, 128), 0),       # H_r > 32
+    ((2, 40, 300, 64, 32, 32, 128), 0),      # 4 receivers per wavefront span 4 KV heads
+    ((2, 40, 300, 64, 30, 10, 128), 0),      # H_r not a multiple of 8
+])
+def test_retrieve_kernel_choice(L, shape, expect):
+    dt, H_s, N, B, H_r, H_kv, d = shape
+    got = L.mf_retrieve_kernel(dt, H_s, N, B, H_r, H_kv, d, A16, A16, H_kv * d, A16, H_r * d)
+    assert got == expect
+
+
+def test_retrieve_kernel_alignment_and_errors(L):
+    args = (2, 40, 8192, 64, 32, 8, 128)
+    ok = L.mf_retrieve_kernel(*args, A16, A16, 8 * 128, A16, 32 * 128)
+    assert ok == 1
+    # V rows must be 16-byte aligned for the matrix-core kernel's direct-to-LDS copies
+    assert L.mf_retrieve_kernel(*args, A16, A16 + 8, 8 * 128, A16, 32 * 128) == 0
+    assert L.mf_retrieve_kernel(*args, A16, A16, 8 * 128 + 4, A16, 32 * 128) == 0
+    assert L.mf_retrieve_kernel(*args, A16 + 8, A16, 8 * 128, A16, 32 * 128) == 0
+    assert L.mf_retrieve_kernel(*args, A16, A16, 8 * 128, A16, 32 * 128 + 4) == 0
+    # shapes mf_retrieve_fused rejects
+    assert L.mf_retrieve_kernel(2, 40, 8192, 64, 30, 8, 128, A16, A16, 1024, A16, 4096) == -mf.MF_ERR_INVALID
+    assert L.mf_retrieve_kernel(2, 40, 8192, 64, 32, 8, 96, A16, A16, 1024, A16, 4096) == -mf.MF_ERR_INVALID
+
+
 def test_last_error_is_thread_local(L):
     import threading
     _retr(L, d=96)

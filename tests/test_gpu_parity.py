@@ -117,23 +117,28 @@ def run_end_to_end(w, device, rows=None, p=None, layer=0, seed=None):
 # ---------------------------------------------------------------------------
 
 RETRIEVE_CASES = [
-    # name, overrides (MFMA kernel unless noted)
-    ("pair14b8b-bf16", dict(N=1000)),                                  # ragged, KS=2, MT=2
-    ("pair8b3b-f16", dict(N=1024)),                                    # G=3
-    ("long32k-f16", dict(N=900)),                                      # B=128
-    ("pair14b8b-bf16", dict(N=300, B=32, H_s=16, H_r=8, H_kv=2)),      # CB=32, KS=1, MT=1
-    ("pair14b8b-bf16", dict(N=520, H_s=64, H_r=32, H_kv=4)),           # max heads, MFMA
-    ("pair8b3b-f16", dict(N=400, d=64)),                               # plain kernel: d=64
-    ("pair14b8b-bf16", dict(N=260, H_r=48, H_kv=8)),                   # plain kernel: H_r>32
-    ("pair14b8b-bf16", dict(N=130, H_r=64, H_kv=16, H_s=64, d=64)),     # plain, max heads
-    ("pair8b3b-f16", dict(N=200, B=16)),                               # plain kernel: B=16
-    ("tiny-f32", dict()),                                              # fp32
-    ("tiny-f32", dict(N=333, B=64, d=128, H_r=8, H_kv=2)),             # fp32, B=64
+    # name, overrides, kernel that must run
+    ("pair14b8b-bf16", dict(N=1000), "mfma"),                            # ragged, 5 sender chunks
+    ("pair8b3b-f16", dict(N=1024), "mfma"),                              # fp16, G = 3, 3 receivers per wave
+    ("long32k-f16", dict(N=900), "mfma"),                                # B = 128
+    ("pair14b8b-bf16", dict(N=300, B=32, H_s=16, H_r=8, H_kv=2), "mfma"),  # B = 32, 1 receiver per wave
+    ("pair14b8b-bf16", dict(N=520, H_s=48, H_r=32, H_kv=4), "mfma"),     # 6 chunks: two tile buffers
+    ("pair8b3b-f16", dict(N=520, H_s=48, H_r=16, H_kv=8), "mfma"),       # fp16, 6 chunks, 2 per wave
+    ("pair14b8b-bf16", dict(N=700, H_s=24, H_r=16, H_kv=4), "mfma"),     # 3 chunks (pair-style plan)
+    ("pair14b8b-bf16", dict(N=333, H_s=8, H_r=24, H_kv=8), "mfma"),      # 1 chunk
+    ("pair8b3b-f16", dict(N=200, B=16), "mfma"),                         # B = 16
+    ("pair14b8b-bf16", dict(N=520, H_s=64, H_r=32, H_kv=4), "plain"),    # H_s > 48
+    ("pair8b3b-f16", dict(N=400, d=64), "plain"),                        # d = 64
+    ("pair14b8b-bf16", dict(N=260, H_r=48, H_kv=8), "plain"),            # H_r > 32
+    ("pair14b8b-bf16", dict(N=130, H_r=64, H_kv=16, H_s=64, d=64), "plain"),  # max heads
+    ("pair14b8b-bf16", dict(N=300, H_r=32, H_kv=32), "plain"),           # G = 1
+    ("tiny-f32", dict(), "plain"),                                       # fp32
+    ("tiny-f32", dict(N=333, B=64, d=128, H_r=8, H_kv=2), "plain"),      # fp32, B = 64
 ]
 
 
-@pytest.mark.parametrize("name,ov", RETRIEVE_CASES)
-def test_retrieve_on_oracle_bsr(gpu, name, ov):
+@pytest.mark.parametrize("name,ov,kernel", RETRIEVE_CASES)
+def test_retrieve_on_oracle_bsr(gpu, name, ov, kernel):
     w = synth.workload(name, **ov)
     say(f"[retrieve] {name} {ov}")
     L = synth.gen_layer(w)                     # CPU generation: small sizes
@@ -144,8 +149,9 @@ def test_retrieve_on_oracle_bsr(gpu, name, ov):
     d_vals = torch.from_numpy(vals).to(gpu).to(tdt)
     d_rp = torch.from_numpy(rp.astype(np.int32)).to(gpu)
     d_ci = torch.from_numpy(ci.astype(np.int32)).to(gpu)
-    O = mf.retrieve_fused(d_rp, d_ci, d_vals, len(ci), L["W"].to(gpu), L["V"].to(gpu),
-                          w.N, w.B)
+    d_W, d_V = L["W"].to(gpu), L["V"].to(gpu)
+    assert mf.retrieve_kernel(d_vals, d_V, d_W, w.N, w.B) == kernel
+    O = mf.retrieve_fused(d_rp, d_ci, d_vals, len(ci), d_W, d_V, w.N, w.B)
     torch.cuda.synchronize()
     rel = check_output(host(O), O_ref, w.dtype)
     say(f"[retrieve] nnzb={len(ci)} max err/max={rel:.3e}")
