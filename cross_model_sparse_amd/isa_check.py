@@ -1,0 +1,251 @@
+"""Static checks of the generated gfx950 code of the retrieval kernels.
+
+The retrieval loop issues its vector-memory operations (direct-to-LDS copies
+and their counter waits) through inline asm, where the compiler neither
+inserts hazard wait states nor tracks outstanding loads.  These checks run on
+`hipcc -S` output and guard the properties that inline asm makes the
+programmer's job:
+
+  scratch      no kernel spills to scratch memory;
+  inflight     no instruction reads or writes a VGPR while it is the
+               destination of a vector load that no `s_waitcnt vmcnt` has
+               retired yet (loads retire in issue order; the walk follows the
+               control-flow graph, takes uniform branches whose condition is a
+               known constant, and assumes a full exec mask);
+  valu_sgpr    no vector-memory instruction reads an SGPR fewer than 5 wait
+               states after a VALU instruction (v_readfirstlane, v_readlane)
+               wrote it;
+  m0_dma       no LDS DMA directly follows the SALU write of M0 it uses.
+
+    python -m cross_model_sparse_amd.isa_check [kernel.hip]
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import sys
+import tempfile
+from collections import deque
+from pathlib import Path
+
+HERE = Path(__file__).resolve().parent
+VMEM = re.compile(r"(global|buffer|flat|scratch)_(load|store|atomic)")
+
+
+def _vregs(tok: str) -> frozenset:
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return frozenset(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return frozenset({int(m.group(1))}) if m else frozenset()
+
+
+def _sgpr_ranges(text: str):
+    for m in re.finditer(r"s\[(\d+):(\d+)\]|\bs(\d+)\b", text):
+        lo = int(m.group(1) or m.group(3))
+        hi = int(m.group(2) or m.group(3))
+        yield lo, hi
+
+
+def _functions(lines):
+    """name -> list of (line number, instruction text) of each kernel body."""
+    out = {}
+    cur = None
+    for ln, raw in enumerate(lines, 1):
+        if re.match(r"^_Z\S+:", raw):
+            cur = raw.split(":")[0]
+            out[cur] = []
+            continue
+        if cur is None:
+            continue
+        if raw.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        s = raw.split(";")[0].strip()
+        if s:
+            out[cur].append((ln, s))
+    return out
+
+
+def _metadata(lines):
+    meta, cur = {}, None
+    for raw in lines:
+        m = re.match(r"\s+\.name:\s+(\S+)", raw)
+        if m:
+            cur = m.group(1)
+            meta.setdefault(cur, {})
+        m = re.match(r"\s+\.(private_segment_fixed_size|vgpr_count):\s+(\d+)", raw)
+        if m and cur:
+            meta[cur][m.group(1)] = int(m.group(2))
+    return meta
+
+
+def _blocks(body):
+    order, blocks, succ = [], {}, {}
+    cur = "@0"
+    order.append(cur)
+    blocks[cur] = []
+    n = 0
+    for ln, s in body:
+        if re.match(r"^\.LBB\S+:$", s):
+            cur = s[:-1]
+            order.append(cur)
+            blocks[cur] = []
+            continue
+        if s.startswith("."):
+            continue
+        blocks[cur].append((ln, s))
+        op = s.split()[0]
+        if op.startswith("s_cbranch") or op in ("s_branch", "s_endpgm"):
+            n += 1
+            cur = f"@{n}"
+            order.append(cur)
+            blocks[cur] = []
+    for k, b in enumerate(order):
+        last = blocks[b][-1][1] if blocks[b] else ""
+        op = last.split()[0] if last else ""
+        nxt = order[k + 1] if k + 1 < len(order) else None
+        if op == "s_branch":
+            succ[b] = [last.split()[1]]
+        elif op == "s_cbranch_execz":        # full exec mask: never taken
+            succ[b] = [nxt] if nxt else []
+        elif op == "s_cbranch_execnz":       # full exec mask: always taken
+            succ[b] = [last.split()[1]]
+        elif op.startswith("s_cbranch"):
+            succ[b] = [last.split()[1]] + ([nxt] if nxt else [])
+        elif op == "s_endpgm":
+            succ[b] = []
+        else:
+            succ[b] = [nxt] if nxt else []
+    return order, blocks, succ
+
+
+def _inflight(body, max_states=64):
+    """Lines touching the destination VGPRs of outstanding vector loads."""
+    order, blocks, succ = _blocks(body)
+    states = {b: set() for b in order}
+    states["@0"].add(((), frozenset()))
+    work = deque(["@0"])
+    bad = {}
+    while work:
+        b = work.popleft()
+        for fifo0, consts0 in list(states[b]):
+            fifo, consts = list(fifo0), dict(consts0)
+            for ln, s in blocks[b]:
+                parts = s.replace(",", " ").split()
+                op, ops = parts[0], parts[1:]
+                if op.startswith("s_") and ops:
+                    dst = ops[0]
+                    if op == "s_mov_b64" and len(ops) > 1 and ops[1] in ("-1", "0"):
+                        consts[dst] = int(ops[1])
+                    elif (op == "s_andn2_b64" and dst == "vcc" and len(ops) > 2
+                          and ops[1] == "exec" and ops[2] in consts):
+                        consts["vcc"] = 1 if consts[ops[2]] == 0 else 0
+                    else:
+                        for k in list(consts):
+                            if k == dst or dst == "vcc" and k == "vcc":
+                                consts.pop(k, None)
+                            elif dst.startswith("s[") and k.startswith("s["):
+                                a = set(range(*map(int, dst[2:-1].split(":"))))
+                                c = set(range(*map(int, k[2:-1].split(":"))))
+                                if a & c:
+                                    consts.pop(k, None)
+                m = re.match(r"s_waitcnt\s+.*vmcnt\((\d+)\)", s)
+                if m:
+                    keep = int(m.group(1))
+                    fifo = fifo[len(fifo) - keep:] if len(fifo) > keep else fifo
+                    continue
+                if VMEM.match(op):
+                    is_load = "load" in op
+                    dest = _vregs(ops[0]) if is_load and "lds" not in op else frozenset()
+                    srcs = ops[1:] if is_load else ops
+                    src = frozenset().union(*[_vregs(t) for t in srcs]) if srcs else frozenset()
+                    for d in fifo:
+                        if src & d or dest & d:
+                            bad.setdefault(ln, s)
+                    fifo.append(dest)
+                    continue
+                if op.startswith("v_") or op.startswith("ds_"):
+                    regs = frozenset().union(*[_vregs(t) for t in ops]) if ops else frozenset()
+                    for d in fifo:
+                        if regs & d:
+                            bad.setdefault(ln, s)
+            out = (tuple(fifo), frozenset(consts.items()))
+            last = blocks[b][-1][1] if blocks[b] else ""
+            nbs = succ[b]
+            if last.startswith("s_cbranch_vccnz") and "vcc" in consts:
+                nbs = nbs[:1] if consts["vcc"] else nbs[1:]
+            elif last.startswith("s_cbranch_vccz") and "vcc" in consts:
+                nbs = nbs[1:] if consts["vcc"] else nbs[:1]
+            for nb in nbs:
+                if nb in states and out not in states[nb] and len(states[nb]) < max_states:
+                    states[nb].add(out)
+                    work.append(nb)
+    return sorted(bad.items())
+
+
+def _linear_hazards(body):
+    insts = [s for _, s in body if not s.startswith(".")]
+    lines = [ln for ln, s in body if not s.startswith(".")]
+    valu_sgpr, m0 = [], []
+    for i, s in enumerate(insts):
+        m = re.match(r"v_read(first)?lane_b32 s(\d+)", s)
+        if m:
+            n, ws = int(m.group(2)), 0
+            for j in range(i + 1, min(len(insts), i + 8)):
+                x = insts[j]
+                if VMEM.match(x.split()[0]) and ws < 5:
+                    if any(lo <= n <= hi for lo, hi in _sgpr_ranges(x)):
+                        valu_sgpr.append((lines[j], x))
+                k = re.match(r"s_nop (\d+)", x)
+                ws += int(k.group(1)) + 1 if k else 1
+        if s.startswith("s_mov_b32 m0") and i + 1 < len(insts):
+            nxt = insts[i + 1]
+            if "lds" in nxt and VMEM.match(nxt.split()[0]):
+                m0.append((lines[i + 1], nxt))
+    return valu_sgpr, m0
+
+
+def check_asm(path: str, pattern: str = "k_retrieve_mfma"):
+    """Findings per kernel whose name contains `pattern`: a dict kernel ->
+    {'scratch': bytes, 'inflight': [...], 'valu_sgpr': [...], 'm0_dma': [...]}."""
+    lines = open(path).read().split("\n")
+    meta = _metadata(lines)
+    out = {}
+    for name, body in _functions(lines).items():
+        if pattern not in name:
+            continue
+        valu_sgpr, m0 = _linear_hazards(body)
+        out[name] = {"scratch": meta.get(name, {}).get("private_segment_fixed_size", 0),
+                     "vgpr": meta.get(name, {}).get("vgpr_count"),
+                     "inflight": _inflight(body), "valu_sgpr": valu_sgpr, "m0_dma": m0}
+    return out
+
+
+def compile_to_asm(src: Path, out: Path) -> None:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", str(HERE / "csrc"), "-I", str(HERE.parent / "include"), "-o", str(out), str(src)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+
+
+def main(argv):
+    src = Path(argv[1]) if len(argv) > 1 else HERE / "csrc" / "k_retrieve.hip"
+    with tempfile.TemporaryDirectory() as td:
+        asm = Path(td) / "k.s"
+        compile_to_asm(src, asm)
+        res = check_asm(str(asm))
+    bad = 0
+    for name, r in sorted(res.items()):
+        n = r["scratch"] + len(r["inflight"]) + len(r["valu_sgpr"]) + len(r["m0_dma"])
+        bad += n
+        print(f"{name[:60]:60s} vgpr {r['vgpr']} scratch {r['scratch']} inflight "
+              f"{len(r['inflight'])} valu_sgpr {len(r['valu_sgpr'])} m0_dma {len(r['m0_dma'])}")
+    print(f"{len(res)} kernels, {bad} findings")
+    return 1 if bad or not res else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

@@ -1,0 +1,97 @@
+"""Static checks of the generated retrieval-kernel code (no GPU needed).
+
+The retrieval loop's copies and counter waits are inline asm, so wait states
+and register lifetimes around them are checked on the compiler's output:
+first the checker itself on planted mistakes, then the real kernels."""
+from __future__ import annotations
+
+import shutil
+
+import pytest
+
+from cross_model_sparse_amd import isa_check
+
+PLANTED = """
+_Zk_retrieve_mfma_demo:
+\tv_readfirstlane_b32 s8, v10
+\tv_readfirstlane_b32 s9, v11
+\tglobal_load_dwordx2 v[20:21], v30, s[8:9]
+\ts_mov_b32 m0, s12
+\tglobal_load_lds_dwordx4 v31, s[8:9]
+\tv_add_u32_e32 v40, v20, v41
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+\t.amdhsa_kernel x
+    .name:           _Zk_retrieve_mfma_demo
+    .private_segment_fixed_size: 16
+    .vgpr_count:     64
+"""
+
+CLEAN = """
+_Zk_retrieve_mfma_demo:
+\tv_readfirstlane_b32 s8, v10
+\tv_readfirstlane_b32 s9, v11
+\ts_nop 4
+\tglobal_load_dwordx2 v[20:21], v30, s[8:9]
+\ts_mov_b32 m0, s12
+\ts_nop 0
+\tglobal_load_lds_dwordx4 v31, s[8:9]
+\ts_waitcnt vmcnt(1)
+\tv_add_u32_e32 v40, v20, v41
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+\t.amdhsa_kernel x
+    .name:           _Zk_retrieve_mfma_demo
+    .private_segment_fixed_size: 0
+    .vgpr_count:     64
+"""
+
+
+def _check_text(tmp_path, text):
+    p = tmp_path / "k.s"
+    p.write_text(text)
+    res = isa_check.check_asm(str(p), pattern="k_retrieve_mfma")
+    assert list(res) == ["_Zk_retrieve_mfma_demo"]
+    return res["_Zk_retrieve_mfma_demo"]
+
+
+def test_checker_flags_planted_mistakes(tmp_path):
+    r = _check_text(tmp_path, PLANTED)
+    assert r["scratch"] == 16
+    # both loads read s[8:9] within 5 wait states of each of its two VALU writes
+    assert len(r["valu_sgpr"]) == 4
+    assert len(r["m0_dma"]) == 1
+    assert [s for _, s in r["inflight"]] == ["v_add_u32_e32 v40, v20, v41"]
+
+
+def test_checker_accepts_the_fixed_forms(tmp_path):
+    r = _check_text(tmp_path, CLEAN)
+    assert r["scratch"] == 0 and not r["valu_sgpr"] and not r["m0_dma"] and not r["inflight"]
+
+
+# one instantiation per code shape: bf16/fp16, 1 or 2 receiver pairs, 2 or 3
+# tile buffers, the four head-mix plans (full groups, remainder 1, 2, 3)
+KERNELS = ["ILb1ELi5ELi2E", "ILb1ELi6ELi2E", "ILb1ELi3ELi1E", "ILb0ELi4ELi2E",
+           "ILb0ELi6ELi1E", "ILb1ELi1ELi1E"]
+
+
+@pytest.fixture(scope="module")
+def retrieve_asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not isa_check.Path("/opt/rocm/bin/hipcc").exists():
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "k_retrieve.s"
+    isa_check.compile_to_asm(isa_check.HERE / "csrc" / "k_retrieve.hip", out)
+    return str(out)
+
+
+@pytest.mark.parametrize("tag", KERNELS)
+def test_retrieve_kernels_have_no_hazards(retrieve_asm, tag):
+    res = isa_check.check_asm(retrieve_asm, pattern="k_retrieve_mfma" + tag)
+    assert len(res) == 1, tag
+    (name, r), = res.items()
+    assert r["scratch"] == 0, name
+    assert not r["valu_sgpr"], r["valu_sgpr"][:3]
+    assert not r["m0_dma"], r["m0_dma"][:3]
+    assert not r["inflight"], r["inflight"][:3]
