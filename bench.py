@@ -15,6 +15,7 @@ retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
 bounded sample of block rows of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
+                    [--copy-ref-mib M]
 """
 from __future__ import annotations
 
@@ -40,7 +41,43 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work for the oracle leg")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (reference "
+                         "kernel for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_retrieve_mfma_pair14b8b_bf16_N8192_traffic.txt")
+KERNEL_SRC = os.path.join(HERE, "cross_model_sparse_amd", "csrc", "k_retrieve.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per retrieval launch measured with hardware counters (two
+    rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by a plain copy
+    of known size), or None when no record exists or the kernel source has
+    changed since it was taken."""
+    try:
+        rec = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+        if rec.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return {"bytes_per_launch": float(rec["hbm_bytes_per_launch"]),
+                "fetch_bytes_per_launch": float(rec["fetch_bytes_per_launch"]),
+                "write_bytes_per_launch": float(rec["write_bytes_per_launch"]),
+                "source": os.path.relpath(TRAFFIC_FILE, HERE)}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -96,6 +133,17 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    if args.copy_ref_mib > 0:
+        # plain copy of known size: the counter-scaling reference
+        n = args.copy_ref_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)         # one elementwise kernel: reads n, writes n bytes
+        torch.cuda.synchronize()
+        log(f"copy reference: {args.copy_ref_mib} MiB read + {args.copy_ref_mib} MiB written per launch")
+        del src, dst
+
     def step(record):
         for x in layers:
             e0, e1, e2, e3 = ev(), ev(), ev(), ev()
@@ -138,6 +186,7 @@ def main():
         return 2.0 * nz * w.H_r * B * B * (w.H_s + w.d)
 
     bytes_step = sum(retr_bytes(nz) for nz in nnzbs)
+    traffic = recorded_traffic()
     flops_step = sum(retr_flops(nz) for nz in nnzbs)
     achieved_gbs = bytes_step * K / t_retr / 1e9
     achieved_tflops = flops_step * K / t_retr / 1e12
@@ -163,7 +212,9 @@ def main():
                    "compute": "bf16 MFMA (W and mixed map as hi+lo bf16), fp32 accumulate",
                    "maps": "structured: sink + band 512 + 4 stripes/head + N(0,1) noise"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "traffic_detail": traffic,
                      "kernel": "k_retrieve_mfma",
                      "bytes_per_launch": bytes_step / L,
                      "mfma_tflops": achieved_tflops,

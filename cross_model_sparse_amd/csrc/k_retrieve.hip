@@ -26,22 +26,29 @@
 //       K = sender heads, N = 16 (row, key) positions; each wavefront owns one
 //       M tile and 4 rows; the fp32 result goes to a double-buffered LDS tile
 //       in the A.V operand layout;
-//     * loads: the V rows of chunk u+1 straight into registers (8-byte loads
-//       from V's own row layout, transposed in registers so that each lane
-//       holds eight consecutive keys of four head-dim columns), then the
-//       [H_s][16 rows][16 keys] tile slice of chunk u+3 into LDS with the
-//       gfx950 direct-to-LDS 16-byte loads (three slices in flight).
+//     * loads: the V rows of chunk u+1, each wavefront copying its own KV
+//       head's 16 x 128 block into its own LDS slot (read back at the start
+//       of the next phase with 8-byte LDS reads and transposed in registers
+//       so that each lane holds eight consecutive keys of four head-dim
+//       columns), then the [H_s][16 rows][16 keys] tile slice of chunk u+3,
+//       both with the gfx950 direct-to-LDS 16-byte loads; the slice copies
+//       sit between the A.V MFMAs (three slices in flight).
 //   Loads return in issue order, so one counter wait per phase ("all but the
-//   newest tile slice") covers both the V registers and the slice needed
-//   next; no barrier drains the prefetch.
+//   newest tile slice") covers both V and the slice needed next; no barrier
+//   drains the prefetch.
 //   bf16: the head mix runs on bf16 MFMA with W split into hi + lo bf16 halves
 //   (W enters exactly); the fp32 mixed map is split the same way into hi + lo
 //   bf16 planes, and A.V runs on bf16 MFMA for both planes against the bf16 V
 //   as stored, so nothing is rounded except the mixed map's hi + lo split
 //   (16 significant bits).  fp16: W and the mixed map are rounded to fp16, V
 //   is used as stored.
-//   Blocks of consecutive rows go to one XCD, so the V rows of their shared
-//   band columns stay in that XCD's L2.
+//   Blocks of consecutive rows go to one XCD, and every row walks its kept
+//   blocks as a rotation of their ascending order chosen so that rows of
+//   equal length meet each band column at the same step (the four 16-row
+//   slices of a row take the block's 16-key chunks in staggered order): the
+//   V rows of a shared band column are then read by all of that XCD's
+//   workgroups within a few phases and come from L2, not HBM.  The output is
+//   written once with non-temporal stores.
 //
 // k_retrieve_simple (every other supported case, including fp32)
 //   One workgroup per (block row, receiver head): the mixed tile is built in
@@ -168,7 +175,7 @@ struct HmPlan {
   static __device__ __forceinline__ int chunk(int b, int q) {
     if (!kBF16) { const int c = 4 * b + q; return c < NCH ? c : -1; }
     if (b < F || R == 3) { const int c = 4 * b + q; return c < NCH ? c : -1; }
-    return q < 2 * R ? 4 * F + (q % R) : -1;
+    return q < 2 * R ? 4 * F + (q % (R ? R : 1)) : -1;
   }
   static __device__ __forceinline__ int half(int b, int w, int q) {
     if (!kBF16) return 0;
@@ -258,11 +265,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
   const int ncc_mask = (1 << lg_ncc) - 1;
-  const int n_chunks = (int)(ke - kb) << lg_ncc;
+  const int cnt = (int)(ke - kb);
+  const int n_chunks = cnt << lg_ncc;
   const int64_t tile = (int64_t)B * B;
+  // The row's kept blocks are walked as a rotation of their ascending order
+  // starting at position (cnt - 1 - I) mod cnt: a row whose list ends in the
+  // band of diagonal columns then meets column J at step J mod cnt, the same
+  // step as every other row of equal length, so neighbouring rows on one XCD
+  // read each band column's V rows at about the same time and share them in
+  // L2 instead of re-fetching them.
+  const int rot = cnt > 0 ? cnt - 1 - I % cnt : 0;
   auto block_of = [&](int x) -> int64_t {       // kept block of chunk x (clamped)
     x = x < n_chunks ? x : n_chunks - 1;
-    return kb + (x >> lg_ncc);
+    const int t = (x >> lg_ncc) + rot;
+    return kb + (t >= cnt ? t - cnt : t);
   };
   auto col_ok = [&](int J) { return J >= 0 && J < T; };
 
@@ -279,9 +295,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     head_off[d] = (unsigned)((s * tile + lane_off) * 2);
   }
   const unsigned smem_lds = lds_addr(smem);
+  // chunk x covers keys 16 * ((x + sub) mod B/16) of its block: the row
+  // slices of one block row take the block's chunks in staggered order
   auto vals_src = [&](int x) -> const unsigned short* {
     const int xc = x < n_chunks ? x : n_chunks - 1;
-    return vals + block_of(x) * H_s * tile + (xc & ncc_mask) * kCB;
+    return vals + block_of(x) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
   };
   auto copy_piece = [&](const unsigned short* src, int slot, int d) {
     if (d < ndv_w) dma16s(head_off[d], src, smem_lds + slot * kStage + (wave + kWaves * d) * 1024);
@@ -315,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   const unsigned short* vlane = V + (int64_t)g * kD + (lane & 15) * 8;
   auto issue_v = [&](int x, int J) {
     const int xc = x < n_chunks ? x : n_chunks - 1;
-    const int key0 = (col_ok(J) ? J : 0) * B + (xc & ncc_mask) * kCB;
+    const int key0 = (col_ok(J) ? J : 0) * B + ((xc + sub) & ncc_mask) * kCB;
     if (key0 + kCB <= N) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) dma16s(v_off, V + (int64_t)(key0 + 4 * m) * ldV, vslot + m * 1024);
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
       const int64_t grow = (int64_t)I * B + sub * kRows + i;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ot + (i * 2 + rp) * kD + d8);
       if (2 * p + rp < RPW && grow < N)
-        *reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)(rbeg + 2 * p + rp) * kD + d8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)(rbeg + 2 * p + rp) * kD + d8));
     }
   }
 }
