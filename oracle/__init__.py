@@ -19,7 +19,10 @@ article on it, aitest123.com/news/zaoi86), step by step in the pages' order:
 4. retrieval: each reuse receiver head is a linear combination of the sender
    heads with learned weights (paper page, "MapFlow System Design" item 3 and
    highlight 2), multiplied by the receiver's own values and accumulated
-   (article, third component; paper page, highlight 4).
+   (article, third component; paper page, highlight 4);
+5. the same compression computed from the sender's Q and K and the per-row
+   log-sum-exp of its scores, without a dense map (article, third section,
+   first component).
 
 Readings of points the pages leave open (the head-map formula in highlight 2 is
 garbled; the statistic, stop rule, tie order, GQA grouping and padding are not
@@ -33,10 +36,12 @@ value).  The loops are deliberately plain: one block, one head at a time.
 Parity pins (tests/test_oracle_pins.py) tie every function to something other
 than itself: dense causal attention from torch's scaled_dot_product_attention,
 brute-force dense decompress-then-matmul, scipy.sparse BSR products, exhaustive
-subset search for the Top-p rule, closed-form block-mass identities and a
-hand-worked example.  No function here is "parity unpinned".
+subset search for the Top-p rule, closed-form block-mass identities, a
+hand-worked example, and for the Q/K compression torch's causal softmax and
+logsumexp, the all-zero-score closed form and plain-loop brute force.  No function here is "parity unpinned".
 """
 from .mapflow_ref import (  # noqa: F401
     n_blocks, block_mass_row, block_mass, topp_row, decision_masses, topp_select,
     bsr_tile, build_bsr, retrieve_row, retrieve, compress, pipeline_row,
+    row_lse, QKMap, compress_qk,
 )

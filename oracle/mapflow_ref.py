@@ -227,3 +227,82 @@ def pipeline_row(A, V, W, B: int, p: float, I: int):
     tiles = [bsr_tile(A, B, I, int(J)) for J in kept]
     O = retrieve_row(I, kept, tiles, W, V, N, B)
     return m, kept, tiles, O
+
+
+# ---------------------------------------------------------------------------
+# 5. compression from the sender's Q and K (no dense map)
+# ---------------------------------------------------------------------------
+#
+# The article's compressor never lays out the full dense attention matrix: it
+# computes the block statistics and then picks blocks (aitest123.com/news/
+# zaoi86, third section, first component).  The sender's map is the causal
+# softmax of its scores, so with Q = [H_s][N][d], K = [H_ks][N][d] (sender head
+# h reads K head h / (H_s / H_ks)), a per-head score scale and the per-row
+# log-sum-exp of the scores, every entry is
+#     A[h][i][j] = exp(scale[h] * q_h,i . k_h,j - lse[h][i]),   j <= i,
+# and both the block masses and the kept tiles follow from Q, K and lse alone.
+# The per-row log-sum-exp is the statistic an attention forward keeps anyway.
+
+def _qk(Q, K):
+    Q = np.asarray(Q, dtype=F64)
+    K = np.asarray(K, dtype=F64)
+    H_s, N, d = Q.shape
+    H_ks = K.shape[0]
+    assert K.shape[1:] == (N, d) and H_s % H_ks == 0
+    return Q, K, H_s // H_ks
+
+
+def row_lse(Q, K, scale, rows=None) -> np.ndarray:
+    """lse[h][i] = log sum_{j <= i} exp(scale[h] * q_h,i . k_h,j), fp64, for the
+    rows ``rows`` (default: all N).  The maximum is subtracted before the
+    exponentials (exact in real arithmetic)."""
+    Q, K, G = _qk(Q, K)
+    sc = np.asarray(scale, dtype=F64)
+    H_s, N, _ = Q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((H_s, len(rows)), dtype=F64)
+    keys = np.arange(N)
+    for h in range(H_s):
+        s = sc[h] * (Q[h, rows] @ K[h // G].T)
+        s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+        m = s.max(axis=1)
+        out[h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
+class QKMap:
+    """The sender's causal map A[H_s][N][N] as a lazy view computed from Q, K,
+    the score scale and the row log-sum-exp; indexing with three slices
+    (heads, rows, columns) returns an fp64 array, zero above the diagonal.
+    The step functions above (block mass, tiles) accept it in place of A."""
+
+    def __init__(self, Q, K, scale, lse):
+        self.Q, self.K, self.G = _qk(Q, K)
+        self.scale = np.asarray(scale, dtype=F64)
+        self.lse = np.asarray(lse, dtype=F64)
+        H_s, N, _ = self.Q.shape
+        assert self.lse.shape == (H_s, N) and self.scale.shape == (H_s,)
+        self.shape = (H_s, N, N)
+        self.dtype = np.dtype(F64)
+
+    def __getitem__(self, idx):
+        hs, rs, cs = idx
+        H_s, N, _ = self.shape
+        heads = np.arange(H_s)[hs]
+        rows = np.arange(N)[rs]
+        cols = np.arange(N)[cs]
+        out = np.empty((len(heads), len(rows), len(cols)), dtype=F64)
+        for a, h in enumerate(heads):
+            s = self.scale[h] * (self.Q[h, rows] @ self.K[h // self.G, cols].T)
+            p = np.exp(s - self.lse[h, rows][:, None])
+            out[a] = np.where(cols[None, :] <= rows[:, None], p, 0.0)
+        return out
+
+
+def compress_qk(Q, K, scale, B: int, p: float, lse=None):
+    """Compression without a dense map: (lse, mass, kept, row_ptr, col_idx,
+    vals) from Q, K and the scale; ``lse`` defaults to the exact row_lse."""
+    lse = row_lse(Q, K, scale) if lse is None else np.asarray(lse, dtype=F64)
+    A = QKMap(Q, K, scale, lse)
+    mass, kept, row_ptr, col_idx, vals = compress(A, B, p)
+    return lse, mass, kept, row_ptr, col_idx, vals

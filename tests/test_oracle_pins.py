@@ -358,3 +358,115 @@ def test_planted_mistakes_are_detected():
     m = np.array([0.5, 0.3, 0.2])
     with pytest.raises(AssertionError):
         selection_ok(m, [0, 1], [0, 2], 0.75)
+
+
+# ---------------------------------------------------------------------------
+# compression from Q and K (no dense map)
+# ---------------------------------------------------------------------------
+
+def _qk_inputs(rng, H_s=4, H_ks=2, N=70, d=16):
+    Q = rng.standard_normal((H_s, N, d))
+    K = rng.standard_normal((H_ks, N, d))
+    scale = rng.uniform(0.05, 0.6, H_s)
+    return Q, K, scale
+
+
+def _torch_causal(Q, K, scale):
+    """Scores, causal softmax and logsumexp in float64 with torch (GQA by
+    repeating each K head over consecutive sender heads)."""
+    H_s, N, _ = Q.shape
+    G = H_s // K.shape[0]
+    q = torch.from_numpy(Q)
+    k = torch.from_numpy(np.repeat(K, G, axis=0))
+    s = torch.einsum("hid,hjd->hij", q, k) * torch.from_numpy(scale)[:, None, None]
+    mask = torch.ones(N, N, dtype=torch.bool).triu_(1)
+    s = s.masked_fill(mask, float("-inf"))
+    return torch.softmax(s, dim=-1).numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+def test_qk_map_matches_torch_causal_softmax():
+    rng = np.random.default_rng(11)
+    Q, K, scale = _qk_inputs(rng)
+    A_ref, lse_ref = _torch_causal(Q, K, scale)
+    lse = oracle.row_lse(Q, K, scale)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+    A = oracle.QKMap(Q, K, scale, lse)
+    np.testing.assert_allclose(A[:, :, :], A_ref, rtol=0, atol=1e-14)
+    # a sampled row range and column range of the lazy view
+    np.testing.assert_allclose(A[1:3, 17:40, 5:33], A_ref[1:3, 17:40, 5:33], rtol=0, atol=1e-14)
+    rows = np.array([0, 9, 69])
+    np.testing.assert_allclose(oracle.row_lse(Q, K, scale, rows=rows), lse_ref[:, rows],
+                               rtol=0, atol=1e-12)
+
+
+def test_qk_zero_scores_closed_form():
+    # all scores zero: every row i attends uniformly to keys 0..i
+    N, B, H_s = 37, 8, 3
+    Q = np.zeros((H_s, N, 4))
+    K = np.ones((1, N, 4))
+    scale = np.full(H_s, 0.5)
+    lse = oracle.row_lse(Q, K, scale)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, N + 1))[None, :].repeat(H_s, 0),
+                               rtol=0, atol=1e-14)
+    mass = oracle.block_mass(oracle.QKMap(Q, K, scale, lse), B)
+    T = oracle.n_blocks(N, B)
+    for I in range(T):
+        for J in range(I + 1):
+            want = sum(len([j for j in range(J * B, min(N, (J + 1) * B)) if j <= i]) / (i + 1)
+                       for i in range(I * B, min(N, (I + 1) * B)))
+            assert abs(mass[I, J] - want) < 1e-13, (I, J)
+
+
+def test_qk_brute_force_tiny():
+    rng = np.random.default_rng(12)
+    H_s, H_ks, N, d = 4, 2, 6, 3
+    Q, K, scale = _qk_inputs(rng, H_s, H_ks, N, d)
+    lse = oracle.row_lse(Q, K, scale)
+    A = oracle.QKMap(Q, K, scale, lse)[:, :, :]
+    for h in range(H_s):
+        g = h // (H_s // H_ks)
+        for i in range(N):
+            s = [scale[h] * sum(Q[h, i, t] * K[g, j, t] for t in range(d)) for j in range(i + 1)]
+            tot = sum(math.exp(x) for x in s)
+            assert abs(lse[h, i] - math.log(tot)) < 1e-12
+            for j in range(N):
+                want = math.exp(s[j]) / tot if j <= i else 0.0
+                assert abs(A[h, i, j] - want) < 1e-14
+
+
+def test_compress_qk_equals_dense_compression():
+    rng = np.random.default_rng(13)
+    Q, K, scale = _qk_inputs(rng, H_s=3, H_ks=1, N=90, d=8)
+    A_ref, _ = _torch_causal(Q, K, scale)
+    for B, p in ((16, 0.9), (32, 0.5), (64, 1.0)):
+        lse, mass, kept, rp, ci, vals = oracle.compress_qk(Q, K, scale, B, p)
+        m2, k2, rp2, ci2, v2 = oracle.compress(A_ref, B, p)
+        np.testing.assert_allclose(mass, m2, rtol=0, atol=1e-12)
+        assert all(np.array_equal(a, b) for a, b in zip(kept, k2))
+        assert np.array_equal(rp, rp2) and np.array_equal(ci, ci2)
+        np.testing.assert_allclose(vals, v2, rtol=0, atol=1e-14)
+
+
+def test_qk_planted_mistakes_are_detected():
+    rng = np.random.default_rng(14)
+    Q, K, scale = _qk_inputs(rng)
+    A_ref, lse_ref = _torch_causal(Q, K, scale)
+    H_s, N, _ = Q.shape
+
+    def lse_with(kidx, causal=True, use_scale=True):
+        out = np.empty((H_s, N))
+        for h in range(H_s):
+            s = (scale[h] if use_scale else 1.0) * (Q[h] @ K[kidx(h)].T)
+            if causal:
+                s = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], s, -np.inf)
+            m = s.max(axis=1)
+            out[h] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        return out
+
+    good = lse_with(lambda h: h // 2)
+    np.testing.assert_allclose(good, lse_ref, rtol=0, atol=1e-12)
+    for bad in (lse_with(lambda h: h % 2),            # interleaved instead of grouped KV heads
+                lse_with(lambda h: h // 2, causal=False),
+                lse_with(lambda h: h // 2, use_scale=False)):
+        with pytest.raises(AssertionError):
+            np.testing.assert_allclose(bad, lse_ref, rtol=0, atol=1e-6)
