@@ -1,0 +1,530 @@
+// Compression from the sender's Q and K, without a dense map.
+//
+// MapFlow's compressor computes block statistics and then picks blocks
+// without first laying out the complete dense attention matrix (article
+// aitest123.com/news/zaoi86, third section, first component).  The sender's
+// causal map is the softmax of its scores, so with the per-row log-sum-exp
+//     A[h][i][j] = exp(scale[h] * q_h,i . k_h,j - lse[h][i]),   j <= i,
+// and the block masses and the kept tiles follow from Q, K and lse:
+//   * k_lse_*      lse[h][i] (online maximum and sum over the causal keys);
+//   * k_mass_qk_*  per-head fp32 sums of A over (16-row tile, column block),
+//                  into a workspace; k_mass_reduce adds tiles and heads in
+//                  fp64 in a fixed order and divides by H_s;
+//   * k_gather_qk_* the kept tiles, recomputed and rounded once.
+// Exponentials run in base 2 on scores pre-multiplied by log2(e).
+//
+// Matrix-core kernels (fp16/bf16, d in {64, 128}; block mass and gather also
+// need B >= 32): a 32 x 32 score tile is S^T = K Q^T on MFMA 32x32x16 with K
+// rows as the A operand (m = key, k = head dim) and Q rows as the B operand
+// (k = head dim, n = query row), so both load straight from their row-major
+// layout and each lane owns one query row: lane l holds row l%32 and the keys
+// 8(e/4) + 4(l/32) + e%4, e = 0..15, of the tile.  Plain kernels cover every
+// other case (fp32, d = 64/128 with B = 16).
+#include "mf_internal.h"
+
+namespace {
+
+using namespace mfd;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRT = 16;                         // rows per partial tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <bool kBF16>
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// plain kernels
+// ---------------------------------------------------------------------------
+
+template <class TT>
+__device__ __forceinline__ float dot_row(const typename TT::S* a, const typename TT::S* b, int d) {
+  float s = 0.f;
+  for (int t = 0; t < d; ++t) s += TT::tof(a[t]) * TT::tof(b[t]);
+  return s;
+}
+
+// one thread per (head, row)
+template <class TT>
+__global__ __launch_bounds__(256) void k_lse_plain(
+    const typename TT::S* __restrict__ Q, const typename TT::S* __restrict__ K, int H_s,
+    int H_ks, int N, int d, const float* __restrict__ scale, float* __restrict__ lse) {
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const int g = h / (H_s / H_ks);
+  const typename TT::S* q = Q + ((int64_t)h * N + i) * d;
+  const typename TT::S* kb = K + (int64_t)g * N * d;
+  const float sc = scale[h] * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    const float x = dot_row<TT>(q, kb + (int64_t)j * d, d) * sc;
+    if (x > m) { l = l * exp2f(m - x) + 1.f; m = x; }
+    else l += exp2f(x - m);
+  }
+  lse[(int64_t)h * N + i] = (m + log2f(l)) * kLn2;
+}
+
+// one workgroup per (16-row tile, head); thread t sums column blocks t, t+256, ...
+template <class TT>
+__global__ __launch_bounds__(256) void k_mass_qk_plain(
+    const typename TT::S* __restrict__ Q, const typename TT::S* __restrict__ K, int H_s,
+    int H_ks, int N, int d, int B, const float* __restrict__ scale,
+    const float* __restrict__ lse, float* __restrict__ part) {
+  const int rt = blockIdx.x, h = blockIdx.y;
+  const int T = (N + B - 1) / B;
+  const int NRT = (N + kRT - 1) / kRT;
+  const int g = h / (H_s / H_ks);
+  const int i0 = rt * kRT, i1 = min(N, i0 + kRT);
+  const int I = i0 / B;
+  const float sc = scale[h] * kLog2e;
+  for (int J = threadIdx.x; J <= I; J += 256) {
+    float acc = 0.f;
+    for (int i = i0; i < i1; ++i) {
+      const typename TT::S* q = Q + ((int64_t)h * N + i) * d;
+      const float l2 = lse[(int64_t)h * N + i] * kLog2e;
+      const int j1 = min(min(N, (J + 1) * B), i + 1);
+      for (int j = J * B; j < j1; ++j)
+        acc += exp2f(dot_row<TT>(q, K + ((int64_t)g * N + j) * d, d) * sc - l2);
+    }
+    part[((int64_t)h * NRT + rt) * T + J] = acc;
+  }
+}
+
+// mass[I][J] = (1/H_s) sum_h sum_{tiles of I} part, fp64 in a fixed order
+__global__ __launch_bounds__(256) void k_mass_reduce(const float* __restrict__ part, int H_s,
+                                                     int N, int B, float* __restrict__ mass) {
+  const int T = (N + B - 1) / B;
+  const int NRT = (N + kRT - 1) / kRT;
+  const int I = blockIdx.x;
+  const int rt0 = I * (B / kRT), rt1 = min(NRT, (I + 1) * (B / kRT));
+  for (int J = threadIdx.x; J < T; J += 256) {
+    float out = 0.f;
+    if (J <= I) {
+      double s = 0.0;
+      for (int h = 0; h < H_s; ++h)
+        for (int rt = rt0; rt < rt1; ++rt) s += (double)part[((int64_t)h * NRT + rt) * T + J];
+      out = (float)(s / (double)H_s);
+    }
+    mass[(int64_t)I * T + J] = out;
+  }
+}
+
+// block row of kept block k: the last I with row_ptr[I] <= k
+__device__ __forceinline__ int row_of(const int32_t* row_ptr, int T, int64_t k) {
+  int lo = 0, hi = T - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)row_ptr[mid] <= k) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// grid-stride over (kept block, head); one thread per tile element
+template <class TT>
+__global__ __launch_bounds__(256) void k_gather_qk_plain(
+    const typename TT::S* __restrict__ Q, const typename TT::S* __restrict__ K, int H_s,
+    int H_ks, int N, int d, int B, const float* __restrict__ scale,
+    const float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ kept, int64_t cap, int32_t* __restrict__ col_idx,
+    typename TT::S* __restrict__ vals) {
+  const int T = (N + B - 1) / B;
+  const int64_t nnzb = row_ptr[T];
+  if (nnzb > cap) return;
+  const int G = H_s / H_ks;
+  for (int64_t u = blockIdx.x; u < nnzb * H_s; u += gridDim.x) {
+    const int64_t k = u / H_s;
+    const int h = (int)(u - k * H_s);
+    const int I = row_of(row_ptr, T, k);
+    const int J = kept[(int64_t)I * T + (k - row_ptr[I])];
+    if (h == 0 && threadIdx.x == 0) col_idx[k] = J;
+    const float sc = scale[h] * kLog2e;
+    for (int e = threadIdx.x; e < B * B; e += 256) {
+      const int r = e / B, c = e % B;
+      const int i = I * B + r, j = J * B + c;
+      float v = 0.f;
+      if (i < N && j <= i) {
+        const float x = dot_row<TT>(Q + ((int64_t)h * N + i) * d,
+                                    K + ((int64_t)(h / G) * N + j) * d, d) * sc;
+        v = exp2f(x - lse[(int64_t)h * N + i] * kLog2e);
+      }
+      vals[((k * H_s + h) * B + r) * B + c] = TT::fromf(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core kernels
+// ---------------------------------------------------------------------------
+
+constexpr int kQkWaves = 8;                     // wavefronts per workgroup
+constexpr int kQkThreads = 64 * kQkWaves;
+constexpr int kQkRows = 32 * kQkWaves;          // query rows per workgroup
+
+// LDS K tile: 32 key rows of D elements, each row padded by 16 bytes so that
+// 16-byte reads of 16 consecutive rows hit distinct banks.
+template <int D>
+struct KTile {
+  static constexpr int kRowBytes = D * 2 + 16;
+  static constexpr int kBytes = 32 * kRowBytes;
+};
+
+// Shared walk of lse and mass: a workgroup owns 256 query rows of head h
+// (wavefront w: rows q0 = R0 + 32w .. +31); K tiles of 32 keys are staged
+// through LDS (double-buffered: every thread loads 16 bytes of the next tile
+// into registers while the current one is in use).  body(kt, c) receives the
+// tile's fp32 scores (in log2 units) for each wavefront whose rows reach key
+// tile kt; mask(...) tells which entries are real.
+template <bool kBF16, int D, class Body>
+__device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
+                                        const unsigned short* __restrict__ K, int h, int g,
+                                        int N, int R0, float sc, unsigned char* smem,
+                                        Body&& body) {
+  constexpr int NKS = D / 16;                   // MFMA K steps
+  constexpr int kRowU4 = D / 8;                 // 16-byte pieces per row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q0 = R0 + 32 * wave;
+  // B operand: this lane's query row (clamped), head-dim chunks 8(l/32) + 16s
+  u32x4 qop[NKS];
+  {
+    const int row = min(q0 + (lane & 31), N - 1);
+    const unsigned short* qr = Q + ((int64_t)h * N + row) * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+  }
+  const int last_row = min(N, R0 + kQkRows) - 1;
+  const int nkt = last_row / 32 + 1;            // key tiles 0..nkt-1
+  // tile loader: 32 rows x D elements = 32 * kRowU4 pieces of 16 bytes
+  const int npieces = 32 * kRowU4;
+  auto load_piece = [&](int kt, int pc) -> u32x4 {
+    const int kr = pc / kRowU4, ch = pc % kRowU4;
+    const int key = min(kt * 32 + kr, N - 1);
+    return *reinterpret_cast<const u32x4*>(K + ((int64_t)g * N + key) * D + 8 * ch);
+  };
+  auto store_piece = [&](int buf, int pc, const u32x4& v) {
+    const int kr = pc / kRowU4, ch = pc % kRowU4;
+    *reinterpret_cast<u32x4*>(smem + buf * KTile<D>::kBytes + kr * KTile<D>::kRowBytes + 16 * ch) = v;
+  };
+  u32x4 stage;                                  // D = 128: 512 pieces, one per thread
+  const bool has_piece = tid < npieces;
+  if (has_piece) store_piece(0, tid, load_piece(0, tid));
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt && has_piece) stage = load_piece(kt + 1, tid);
+    if (kt * 32 <= q0 + 31 && q0 < N) {         // some key of the tile is causal for these rows
+      const unsigned char* kb = smem + buf * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
+      f32x16 c = {};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kb + 32 * s), qop[s], c);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c[e] *= sc;
+      body(kt, c);
+    }
+    if (kt + 1 < nkt) {
+      if (has_piece) store_piece(buf ^ 1, tid, stage);
+      __syncthreads();
+    }
+  }
+}
+
+// key of output element e of this lane within a tile
+__device__ __forceinline__ int tile_key(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+template <bool kBF16, int D>
+__global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
+    int H_ks, int N, const float* __restrict__ scale, float* __restrict__ lse) {
+  __shared__ __align__(16) unsigned char smem[2 * KTile<D>::kBytes];
+  const int ngrp = (N + kQkRows - 1) / kQkRows;
+  const int h = blockIdx.x / ngrp;
+  const int R0 = (ngrp - 1 - blockIdx.x % ngrp) * kQkRows;   // longest rows first
+  const int g = h / (H_s / H_ks);
+  const int lane = threadIdx.x & 63;
+  const int q0 = R0 + 32 * (threadIdx.x >> 6);
+  const int row = q0 + (lane & 31);
+  float m = -INFINITY, l = 0.f;
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, scale[h] * kLog2e, smem, [&](int kt, const f32x16& c) {
+    float x[16];
+    float mx = m;
+    if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { x[e] = c[e]; mx = fmaxf(mx, x[e]); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = kt * 32 + tile_key(lane, e);
+        x[e] = (j <= row && j < N) ? c[e] : -INFINITY;
+        mx = fmaxf(mx, x[e]);
+      }
+    }
+    if (mx > -INFINITY) {
+      float s = l * exp2f(m - mx);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += exp2f(x[e] - mx);
+      l = s;
+      m = mx;
+    }
+  });
+  // lanes l and l+32 hold the same row: merge their (max, sum)
+  const float m2 = __shfl_xor(m, 32);
+  const float l2 = __shfl_xor(l, 32);
+  const float mm = fmaxf(m, m2);
+  const float ll = (m > -INFINITY ? l * exp2f(m - mm) : 0.f) + (m2 > -INFINITY ? l2 * exp2f(m2 - mm) : 0.f);
+  if (lane < 32 && row < N) lse[(int64_t)h * N + row] = (mm + log2f(ll)) * kLn2;
+}
+
+template <bool kBF16, int D>
+__global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
+    int H_ks, int N, int B, const float* __restrict__ scale, const float* __restrict__ lse,
+    float* __restrict__ part) {
+  __shared__ __align__(16) unsigned char smem[2 * KTile<D>::kBytes];
+  const int T = (N + B - 1) / B;
+  const int NRT = (N + kRT - 1) / kRT;
+  const int ngrp = (N + kQkRows - 1) / kQkRows;
+  const int h = blockIdx.x / ngrp;
+  const int R0 = (ngrp - 1 - blockIdx.x % ngrp) * kQkRows;
+  const int g = h / (H_s / H_ks);
+  const int lane = threadIdx.x & 63;
+  const int q0 = R0 + 32 * (threadIdx.x >> 6);
+  const int row = q0 + (lane & 31);
+  const float l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
+  const int tpb = B / 32;                        // key tiles per column block
+  float acc = 0.f;
+  // sums of the lanes of one 16-row tile: lanes {0..15, 32..47} and {16..31, 48..63}
+  auto flush = [&](int J) {
+    float v = acc;
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 32);
+    const int rt = q0 / kRT + ((lane >> 4) & 1);
+    if ((lane == 0 || lane == 16) && rt * kRT < N) part[((int64_t)h * NRT + rt) * T + J] = v;
+    acc = 0.f;
+  };
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, scale[h] * kLog2e, smem, [&](int kt, const f32x16& c) {
+    if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc += exp2f(c[e] - l2);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = kt * 32 + tile_key(lane, e);
+        acc += (j <= row && j < N && row < N) ? exp2f(c[e] - l2) : 0.f;
+      }
+    }
+    const int J = kt / tpb;
+    // the block's last tile, or the last tile these rows reach
+    if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) flush(J);
+  });
+}
+
+// one wavefront per (kept block, head); per (32-row, 32-key) sub-tile
+template <bool kBF16, int D>
+__global__ __launch_bounds__(256) void k_gather_qk_mfma(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
+    int H_ks, int N, int B, const float* __restrict__ scale, const float* __restrict__ lse,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ kept, int64_t cap,
+    int32_t* __restrict__ col_idx, unsigned short* __restrict__ vals) {
+  constexpr int NKS = D / 16;
+  const int T = (N + B - 1) / B;
+  const int64_t nnzb = row_ptr[T];
+  if (nnzb > cap) return;
+  const int G = H_s / H_ks;
+  const int lane = threadIdx.x & 63;
+  const int nsub = B / 32;
+  const int64_t items = nnzb * H_s;
+  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < items; u += (int64_t)gridDim.x * 4) {
+    const int64_t k = u / H_s;
+    const int h = (int)(u - k * H_s);
+    const int I = row_of(row_ptr, T, k);
+    const int J = kept[(int64_t)I * T + (k - row_ptr[I])];
+    if (h == 0 && lane == 0) col_idx[k] = J;
+    const float sc = scale[h] * kLog2e;
+    const unsigned short* kbase = K + (int64_t)(h / G) * N * D;
+    unsigned short* tile = vals + (k * H_s + h) * (int64_t)B * B;
+    for (int qs = 0; qs < nsub; ++qs) {
+      const int row = I * B + qs * 32 + (lane & 31);
+      const bool row_ok = row < N;
+      u32x4 qop[NKS];
+      {
+        const unsigned short* qr = Q + ((int64_t)h * N + min(row, N - 1)) * D + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+      }
+      const float l2 = row_ok ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
+      for (int ks = 0; ks < nsub; ++ks) {
+        const int key0 = J * B + ks * 32;
+        f32x16 c = {};
+        if (key0 <= I * B + qs * 32 + 31) {     // not entirely above the diagonal
+          const unsigned short* kr = kbase + (int64_t)min(key0 + (lane & 31), N - 1) * D + 8 * (lane >> 5);
+#pragma unroll
+          for (int s = 0; s < NKS; ++s)
+            c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kr + 16 * s), qop[s], c);
+        }
+        // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          unsigned short hv[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int e = 4 * e4 + t;
+            const int j = key0 + tile_key(lane, e);
+            const float v = (row_ok && j <= row) ? exp2f(c[e] * sc - l2) : 0.f;
+            hv[t] = kBF16 ? f32_to_bf16(v) : f32_to_f16(v);
+          }
+          const int col = ks * 32 + 8 * e4 + 4 * (lane >> 5);
+          *reinterpret_cast<u32x2*>(tile + (int64_t)(qs * 32 + (lane & 31)) * B + col) =
+              u32x2{(unsigned)hv[0] | ((unsigned)hv[1] << 16), (unsigned)hv[2] | ((unsigned)hv[3] << 16)};
+        }
+      }
+    }
+  }
+}
+
+bool qk_mfma(int dt, int d, const void* Q, const void* K) {
+  return dt != MF_F32 && (d == 64 || d == 128) &&
+         (reinterpret_cast<uintptr_t>(Q) & 15) == 0 && (reinterpret_cast<uintptr_t>(K) & 15) == 0;
+}
+
+template <class TT>
+hipError_t lse_plain(const void* Q, const void* K, int H_s, int H_ks, int N, int d,
+                     const float* scale, float* lse, hipStream_t st) {
+  using S = typename TT::S;
+  hipLaunchKernelGGL((k_lse_plain<TT>), dim3((N + 255) / 256, H_s), dim3(256), 0, st,
+                     reinterpret_cast<const S*>(Q), reinterpret_cast<const S*>(K), H_s, H_ks,
+                     N, d, scale, lse);
+  return hipGetLastError();
+}
+
+template <class TT>
+hipError_t mass_plain(const void* Q, const void* K, int H_s, int H_ks, int N, int d, int B,
+                      const float* scale, const float* lse, float* part, hipStream_t st) {
+  using S = typename TT::S;
+  hipLaunchKernelGGL((k_mass_qk_plain<TT>), dim3((N + kRT - 1) / kRT, H_s), dim3(256), 0, st,
+                     reinterpret_cast<const S*>(Q), reinterpret_cast<const S*>(K), H_s, H_ks,
+                     N, d, B, scale, lse, part);
+  return hipGetLastError();
+}
+
+template <class TT>
+hipError_t gather_plain(const void* Q, const void* K, int H_s, int H_ks, int N, int d, int B,
+                        const float* scale, const float* lse, const int32_t* row_ptr,
+                        const int32_t* kept, int64_t cap, int32_t* col_idx, void* vals,
+                        hipStream_t st) {
+  using S = typename TT::S;
+  const int T = mf::blocks_of(N, B);
+  const int64_t ub = std::min<int64_t>(cap, (int64_t)T * (T + 1) / 2) * H_s;
+  if (ub <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gather_qk_plain<TT>), dim3((int)std::min<int64_t>(ub, 8192)), dim3(256), 0,
+                     st, reinterpret_cast<const S*>(Q), reinterpret_cast<const S*>(K), H_s, H_ks,
+                     N, d, B, scale, lse, row_ptr, kept, cap, col_idx, reinterpret_cast<S*>(vals));
+  return hipGetLastError();
+}
+
+template <bool kBF16>
+hipError_t lse_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, int d,
+                    const float* scale, float* lse, hipStream_t st) {
+  auto q = reinterpret_cast<const unsigned short*>(Q);
+  auto k = reinterpret_cast<const unsigned short*>(K);
+  const dim3 grid(H_s * ((N + kQkRows - 1) / kQkRows));
+  if (d == 128) hipLaunchKernelGGL((k_lse_mfma<kBF16, 128>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, scale, lse);
+  else hipLaunchKernelGGL((k_lse_mfma<kBF16, 64>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, scale, lse);
+  return hipGetLastError();
+}
+
+template <bool kBF16>
+hipError_t mass_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, int d, int B,
+                     const float* scale, const float* lse, float* part, hipStream_t st) {
+  auto q = reinterpret_cast<const unsigned short*>(Q);
+  auto k = reinterpret_cast<const unsigned short*>(K);
+  const dim3 grid(H_s * ((N + kQkRows - 1) / kQkRows));
+  if (d == 128) hipLaunchKernelGGL((k_mass_qk_mfma<kBF16, 128>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, B, scale, lse, part);
+  else hipLaunchKernelGGL((k_mass_qk_mfma<kBF16, 64>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, B, scale, lse, part);
+  return hipGetLastError();
+}
+
+template <bool kBF16>
+hipError_t gather_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, int d, int B,
+                       const float* scale, const float* lse, const int32_t* row_ptr,
+                       const int32_t* kept, int64_t cap, int32_t* col_idx, void* vals,
+                       hipStream_t st) {
+  const int T = mf::blocks_of(N, B);
+  const int64_t ub = std::min<int64_t>(cap, (int64_t)T * (T + 1) / 2) * H_s;
+  if (ub <= 0) return hipSuccess;
+  const dim3 grid((unsigned)std::min<int64_t>((ub + 3) / 4, 16384));
+  auto q = reinterpret_cast<const unsigned short*>(Q);
+  auto k = reinterpret_cast<const unsigned short*>(K);
+  auto v = reinterpret_cast<unsigned short*>(vals);
+  if (d == 128) hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, 128>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, B, scale, lse, row_ptr, kept, cap, col_idx, v);
+  else hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, 64>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, B, scale, lse, row_ptr, kept, cap, col_idx, v);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace mf {
+
+hipError_t launch_row_lse(const void* Q, const void* K, int dt, int H_s, int H_ks, int N, int d,
+                          const float* scale, float* lse, hipStream_t st) {
+  if (qk_mfma(dt, d, Q, K))
+    return dt == MF_BF16 ? lse_mfma<true>(Q, K, H_s, H_ks, N, d, scale, lse, st)
+                         : lse_mfma<false>(Q, K, H_s, H_ks, N, d, scale, lse, st);
+  if (dt == MF_F32) return lse_plain<mfd::TF32>(Q, K, H_s, H_ks, N, d, scale, lse, st);
+  if (dt == MF_F16) return lse_plain<mfd::TF16>(Q, K, H_s, H_ks, N, d, scale, lse, st);
+  return lse_plain<mfd::TBF16>(Q, K, H_s, H_ks, N, d, scale, lse, st);
+}
+
+size_t block_mass_qk_workspace_bytes(int H_s, int N, int B) {
+  return (size_t)H_s * (size_t)((N + kRT - 1) / kRT) * (size_t)blocks_of(N, B) * sizeof(float);
+}
+
+hipError_t launch_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                                int dt, int H_s, int H_ks, int N, int d, int B, float* mass,
+                                void* workspace, hipStream_t st) {
+  float* part = reinterpret_cast<float*>(workspace);
+  hipError_t e;
+  if (qk_mfma(dt, d, Q, K) && B >= 32)
+    e = dt == MF_BF16 ? mass_mfma<true>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st)
+                      : mass_mfma<false>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
+  else if (dt == MF_F32) e = mass_plain<mfd::TF32>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
+  else if (dt == MF_F16) e = mass_plain<mfd::TF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
+  else e = mass_plain<mfd::TBF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_mass_reduce, dim3(blocks_of(N, B)), dim3(256), 0, st, part, H_s, N, B, mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                            int dt, int H_s, int H_ks, int N, int d, int B,
+                            const int32_t* row_ptr, const int32_t* kept, int64_t cap,
+                            int32_t* col_idx, void* vals, hipStream_t st) {
+  if (qk_mfma(dt, d, Q, K) && B >= 32 && (reinterpret_cast<uintptr_t>(vals) & 7) == 0)
+    return dt == MF_BF16
+               ? gather_mfma<true>(Q, K, H_s, H_ks, N, d, B, scale, lse, row_ptr, kept, cap, col_idx, vals, st)
+               : gather_mfma<false>(Q, K, H_s, H_ks, N, d, B, scale, lse, row_ptr, kept, cap, col_idx, vals, st);
+  if (dt == MF_F32)
+    return gather_plain<mfd::TF32>(Q, K, H_s, H_ks, N, d, B, scale, lse, row_ptr, kept, cap, col_idx, vals, st);
+  if (dt == MF_F16)
+    return gather_plain<mfd::TF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, row_ptr, kept, cap, col_idx, vals, st);
+  return gather_plain<mfd::TBF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, row_ptr, kept, cap, col_idx, vals, st);
+}
+
+}  // namespace mf

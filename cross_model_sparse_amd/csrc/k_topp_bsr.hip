@@ -238,10 +238,8 @@ hipError_t launch_gather_t(int vec, const void* A, int H_s, int N, int B,
 
 namespace mf {
 
-hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
-                           int N, int B, float p, int32_t* row_ptr,
-                           int32_t* col_idx, void* vals, int64_t cap_nnzb,
-                           void* workspace, hipStream_t st) {
+hipError_t launch_select_scan(const float* mass, int N, int B, float p, int32_t* row_ptr,
+                              void* workspace, hipStream_t st) {
   const int T = blocks_of(N, B);
   int32_t* kept = reinterpret_cast<int32_t*>(workspace);
   int32_t* count = kept + (int64_t)T * T;
@@ -251,7 +249,15 @@ hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, st, count, T,
                      row_ptr);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
+                           int N, int B, float p, int32_t* row_ptr,
+                           int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                           void* workspace, hipStream_t st) {
+  const int32_t* kept = reinterpret_cast<const int32_t*>(workspace);
+  hipError_t e = launch_select_scan(mass, N, B, p, row_ptr, workspace, st);
   if (e != hipSuccess) return e;
   int vec = row_vec_bytes(A, N, B, dtype_bytes(dt));
   while (vec > dtype_bytes(dt) && (reinterpret_cast<uintptr_t>(vals) % vec) != 0) vec >>= 1;

@@ -134,6 +134,94 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
   return MF_OK;
 }
 
+// Shape checks shared by the calls that read Q and K.
+static int check_qk(const char* fn, int dtype, int H_s, int H_ks, int N, int d, int B) {
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (H_ks < 1 || H_s % H_ks != 0)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": H_ks = %lld does not divide H_s", H_ks));
+  if (d != 64 && d != 128) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": d must be 64 or 128 (got %lld)", d));
+  return MF_OK;
+}
+
+int mf_row_lse(const void* Q, const void* K, int dtype, int H_s, int H_ks, int N, int d,
+               const float* scale, float* lse, void* stream) {
+  const char* fn = "mf_row_lse";
+  // any valid block size passes the shared geometry check
+  int st = check_qk(fn, dtype, H_s, H_ks, N, d, 16);
+  if (st != MF_OK) return st;
+  if (!Q || !K || !scale || !lse) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  return mf::hip_check(mf::launch_row_lse(Q, K, dtype, H_s, H_ks, N, d, scale, lse,
+                                          (hipStream_t)stream), "mf_row_lse launch");
+}
+
+size_t mf_block_mass_qk_workspace_bytes(int H_s, int N, int B) {
+  if (H_s < 1 || H_s > 64 || N < 1 || !valid_block(B)) return 0;
+  return mf::block_mass_qk_workspace_bytes(H_s, N, B);
+}
+
+int mf_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                     int dtype, int H_s, int H_ks, int N, int d, int B, float* mass,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mf_block_mass_qk";
+  int st = check_qk(fn, dtype, H_s, H_ks, N, d, B);
+  if (st != MF_OK) return st;
+  if (!Q || !K || !scale || !lse || !mass || !workspace)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  const size_t need = mf::block_mass_qk_workspace_bytes(H_s, N, B);
+  if (workspace_bytes < need)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          (long long)workspace_bytes, (long long)need));
+  return mf::hip_check(mf::launch_block_mass_qk(Q, K, scale, lse, dtype, H_s, H_ks, N, d, B, mass,
+                                                workspace, (hipStream_t)stream),
+                       "mf_block_mass_qk launch");
+}
+
+int mf_topp_select_bsr_qk(const float* mass, const void* Q, const void* K,
+                          const float* scale, const float* lse, int dtype, int H_s,
+                          int H_ks, int N, int d, int B, float p, int32_t* row_ptr,
+                          int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                          int64_t* nnzb_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "mf_topp_select_bsr_qk";
+  int st = check_qk(fn, dtype, H_s, H_ks, N, d, B);
+  if (st != MF_OK) return st;
+  if (!mass || !Q || !K || !scale || !lse || !row_ptr || !workspace)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (cap_nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": cap_nnzb < 0");
+  if (cap_nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with cap_nnzb > 0");
+  if (!(p > 0.0f && p <= 1.0f))  // also rejects NaN
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": p must be in (0, 1]");
+  const int T = mf::blocks_of(N, B);
+  if (T > 4096)
+    return mf::fail(MF_ERR_UNSUPPORTED, std::string(fn) + fmt(": T = %lld block rows > 4096", T));
+  if (workspace_bytes < mf_topp_workspace_bytes(N, B))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          (long long)workspace_bytes,
+                                                          (long long)mf_topp_workspace_bytes(N, B)));
+  hipStream_t s = (hipStream_t)stream;
+  st = mf::hip_check(mf::launch_select_scan(mass, N, B, p, row_ptr, workspace, s),
+                     "mf_topp_select_bsr_qk selection launch");
+  if (st != MF_OK) return st;
+  st = mf::hip_check(mf::launch_gather_qk(Q, K, scale, lse, dtype, H_s, H_ks, N, d, B, row_ptr,
+                                          reinterpret_cast<const int32_t*>(workspace), cap_nnzb,
+                                          col_idx, vals, s),
+                     "mf_topp_select_bsr_qk gather launch");
+  if (st != MF_OK || !nnzb_out) return st;
+  int32_t nnzb = 0;
+  st = mf::hip_check(hipMemcpyAsync(&nnzb, row_ptr + T, sizeof nnzb, hipMemcpyDeviceToHost, s),
+                     "mf_topp_select_bsr_qk nnzb read-back");
+  if (st != MF_OK) return st;
+  st = mf::hip_check(hipStreamSynchronize(s), "mf_topp_select_bsr_qk synchronise");
+  if (st != MF_OK) return st;
+  *nnzb_out = nnzb;
+  if (nnzb > cap_nnzb)
+    return mf::fail(MF_ERR_CAPACITY, std::string(fn) + fmt(": nnzb = %lld exceeds cap_nnzb = %lld",
+                                                           nnzb, cap_nnzb));
+  return MF_OK;
+}
+
 size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype) {
   if (N < 1 || !valid_block(B) || H_kv < 1 || !valid_dtype(dtype)) return 0;
   return mf::retrieve_workspace_bytes(N, B, H_kv, d, dtype);

@@ -28,6 +28,21 @@ hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
                            int N, int B, float p, int32_t* row_ptr,
                            int32_t* col_idx, void* vals, int64_t cap_nnzb,
                            void* workspace, hipStream_t st);
+// Top-p selection and row_ptr scan only (kept[T][T] and counts in workspace).
+hipError_t launch_select_scan(const float* mass, int N, int B, float p, int32_t* row_ptr,
+                              void* workspace, hipStream_t st);
+// Compression from Q and K (k_qk.hip).
+hipError_t launch_row_lse(const void* Q, const void* K, int dt, int H_s, int H_ks, int N, int d,
+                          const float* scale, float* lse, hipStream_t st);
+size_t block_mass_qk_workspace_bytes(int H_s, int N, int B);
+hipError_t launch_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                                int dt, int H_s, int H_ks, int N, int d, int B, float* mass,
+                                void* workspace, hipStream_t st);
+// Kept tiles recomputed from Q, K, lse; row_ptr and kept[T][T] from launch_select_scan.
+hipError_t launch_gather_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                            int dt, int H_s, int H_ks, int N, int d, int B,
+                            const int32_t* row_ptr, const int32_t* kept, int64_t cap,
+                            int32_t* col_idx, void* vals, hipStream_t st);
 int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     const void* vals, int64_t nnzb, int dt, int H_s, int N,
                     int B, const float* W, int H_r, const void* V, int H_kv,

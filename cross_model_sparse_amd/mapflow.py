@@ -23,8 +23,9 @@ MF_F32, MF_F16, MF_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_BF16}
 
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
-            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_retrieve_workspace_bytes",
-            "mf_retrieve_kernel", "mf_retrieve_fused")
+            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
+            "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
+            "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused")
 
 
 class MapflowError(RuntimeError):
@@ -72,6 +73,17 @@ def load() -> ctypes.CDLL:
     L.mf_topp_select_bsr.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_f, c_vp,
                                      c_vp, c_vp, c_i64, ctypes.POINTER(c_i64), c_vp,
                                      c_sz, c_vp]
+    L.mf_row_lse.restype = c_int
+    L.mf_row_lse.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp]
+    L.mf_block_mass_qk_workspace_bytes.restype = c_sz
+    L.mf_block_mass_qk_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.mf_block_mass_qk.restype = c_int
+    L.mf_block_mass_qk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
+                                   c_int, c_vp, c_vp, c_sz, c_vp]
+    L.mf_topp_select_bsr_qk.restype = c_int
+    L.mf_topp_select_bsr_qk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                        c_int, c_int, c_f, c_vp, c_vp, c_vp, c_i64,
+                                        ctypes.POINTER(c_i64), c_vp, c_sz, c_vp]
     L.mf_retrieve_workspace_bytes.restype = c_sz
     L.mf_retrieve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
     L.mf_retrieve_kernel.restype = c_int
@@ -230,6 +242,100 @@ def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Ten
                                     V.stride(0), _ptr(out), out.stride(0), _ptr(workspace),
                                     ws_bytes, _stream(stream)))
     return out
+
+
+def _qk_shapes(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor):
+    _need_cuda(Q, K, scale)
+    if Q.dim() != 3 or K.dim() != 3 or not Q.is_contiguous() or not K.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "Q and K must be contiguous [H][N][d] tensors")
+    if K.dtype != Q.dtype or K.shape[1:] != Q.shape[1:]:
+        raise MapflowError(MF_ERR_INVALID, "K must match Q in dtype, N and d")
+    if scale.dtype != torch.float32 or scale.numel() != Q.shape[0] or not scale.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "scale must be a contiguous float32 [H_s] tensor")
+    return Q.shape[0], K.shape[0], Q.shape[1], Q.shape[2]
+
+
+def row_lse(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor,
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """lse[H_s][N] fp32: per-row log-sum-exp of the causal scores (mf_row_lse)."""
+    H_s, H_ks, N, d = _qk_shapes(Q, K, scale)
+    if out is None:
+        out = torch.empty(H_s, N, dtype=torch.float32, device=Q.device)
+    _check(load().mf_row_lse(_ptr(Q), _ptr(K), _dcode(Q), H_s, H_ks, N, d, _ptr(scale),
+                             _ptr(out), _stream(stream)))
+    return out
+
+
+def block_mass_qk_workspace_bytes(H_s: int, N: int, B: int) -> int:
+    return int(load().mf_block_mass_qk_workspace_bytes(H_s, N, B))
+
+
+def block_mass_qk(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor, lse: torch.Tensor,
+                  B: int, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """mass[T][T] fp32 from Q, K, scale and lse, without a dense map (mf_block_mass_qk)."""
+    H_s, H_ks, N, d = _qk_shapes(Q, K, scale)
+    _need_cuda(lse)
+    T = -(-N // B)
+    if out is None:
+        out = torch.empty(T, T, dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, block_mass_qk_workspace_bytes(H_s, N, B)),
+                                dtype=torch.uint8, device=Q.device)
+    _check(load().mf_block_mass_qk(_ptr(Q), _ptr(K), _ptr(scale), _ptr(lse), _dcode(Q), H_s,
+                                   H_ks, N, d, B, _ptr(out), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
+    return out
+
+
+def topp_select_bsr_qk(mass: torch.Tensor, Q: torch.Tensor, K: torch.Tensor,
+                       scale: torch.Tensor, lse: torch.Tensor, B: int, p: float,
+                       cap_nnzb: int | None = None, row_ptr=None, col_idx=None, vals=None,
+                       workspace=None, sync: bool = True, stream=None):
+    """Top-p selection + BSR build with the kept tiles recomputed from Q, K and
+    lse (mf_topp_select_bsr_qk).  Same returns and capacity handling as
+    topp_select_bsr."""
+    H_s, H_ks, N, d = _qk_shapes(Q, K, scale)
+    _need_cuda(mass, lse)
+    T = -(-N // B)
+    L = load()
+    dev = Q.device
+    if workspace is None:
+        workspace = torch.empty(topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    args = (_ptr(mass), _ptr(Q), _ptr(K), _ptr(scale), _ptr(lse), _dcode(Q), H_s, H_ks, N, d,
+            B, float(p))
+    if cap_nnzb is None:
+        n = ctypes.c_int64(0)
+        st = L.mf_topp_select_bsr_qk(*args, _ptr(row_ptr), None, None, 0, ctypes.byref(n),
+                                     _ptr(workspace), workspace.numel(), _stream(stream))
+        if st not in (MF_OK, MF_ERR_CAPACITY):
+            _check(st)
+        cap_nnzb = int(n.value)
+    if col_idx is None:
+        col_idx = torch.empty(max(cap_nnzb, 1), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((max(cap_nnzb, 1), H_s, B, B), dtype=Q.dtype, device=dev)
+    n = ctypes.c_int64(-1)
+    st = L.mf_topp_select_bsr_qk(*args, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(cap_nnzb),
+                                 ctypes.byref(n) if sync else None, _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check(st, int(n.value))
+    nnzb = int(n.value) if sync else None
+    return row_ptr, col_idx, vals, nnzb
+
+
+def compress_qk(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor, B: int, p: float,
+                lse: torch.Tensor | None = None, cap_nnzb: int | None = None, stream=None):
+    """Compression without a dense map: (lse, mass, row_ptr, col_idx, vals, nnzb);
+    lse is computed with row_lse when not given."""
+    if lse is None:
+        lse = row_lse(Q, K, scale, stream=stream)
+    mass = block_mass_qk(Q, K, scale, lse, B, stream=stream)
+    row_ptr, col_idx, vals, nnzb = topp_select_bsr_qk(mass, Q, K, scale, lse, B, p,
+                                                      cap_nnzb=cap_nnzb, stream=stream)
+    return lse, mass, row_ptr, col_idx, vals, nnzb
 
 
 def compress(A: torch.Tensor, B: int, p: float, cap_nnzb: int | None = None, stream=None):

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 1
+#define MF_ABI_VERSION 2
 
 typedef enum {
   MF_OK = 0,
@@ -127,6 +127,61 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
                        int32_t* col_idx, void* vals, int64_t cap_nnzb,
                        int64_t* nnzb_out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Compression without a dense map (article, third section, first component:
+ * the block statistics and the kept blocks are obtained without first laying
+ * out the complete dense attention matrix).
+ *
+ * The sender layer's causal attention is the softmax of its scores,
+ *   s_h[i][j] = scale[h] * (q_h,i . k_h,j),   j <= i,
+ *   A[h][i][j] = exp(s_h[i][j] - lse[h][i]),  lse[h][i] = log sum_{j<=i} exp(s_h[i][j]),
+ * with Q = [H_s][N][d] and K = [H_ks][N][d] (contiguous rows of d elements,
+ * dtype `dtype`); sender head h reads K head h / (H_s / H_ks).  lse is the
+ * per-row statistic an attention forward keeps; mf_row_lse computes it when
+ * the caller does not have it.  The three calls below give the same block
+ * masses and kept tiles as mf_block_mass / mf_topp_select_bsr on that map,
+ * computed from Q, K, scale and lse; A is never formed.  Scores are
+ * accumulated in fp32 from the stored Q and K; exponentials are fp32.
+ *
+ * Common arguments: Q, K device; scale device, [H_s] float32; lse device,
+ * [H_s][N] float32; d in {64, 128}; H_ks >= 1 dividing H_s.  Errors:
+ * MF_ERR_INVALID for null pointers, N < 1, B not in {16,32,64,128}, H_s not
+ * in [1,64], H_ks not dividing H_s, d not in {64,128} or an unknown dtype.
+ */
+
+/* lse[h][i] for every sender head and row (device, [H_s][N] float32). */
+int mf_row_lse(const void* Q, const void* K, int dtype, int H_s, int H_ks, int N, int d,
+               const float* scale, float* lse, void* stream);
+
+/* Workspace bytes mf_block_mass_qk needs: per-head partial sums over 16-row
+ * tiles, H_s * ceil(N/16) * T float32. */
+size_t mf_block_mass_qk_workspace_bytes(int H_s, int N, int B);
+
+/*
+ *   mass[I][J] = (1/H_s) * sum_h sum_{i in I, i<N} sum_{j in J, j<=i} exp(s_h[i][j] - lse[h][i])
+ * for J <= I, 0 for J > I (device, [T][T] float32, written completely).  Each
+ * head's sum over a 16-row tile and a column block is an fp32 sum; the tiles
+ * and heads of a block are combined in fp64 in a fixed order, so the result
+ * is bit-reproducible.  workspace: device, >= mf_block_mass_qk_workspace_bytes.
+ */
+int mf_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
+                     int dtype, int H_s, int H_ks, int N, int d, int B, float* mass,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-level Top-p selection and BSR build as mf_topp_select_bsr (same rule,
+ * same row_ptr / col_idx / capacity / nnzb_out / workspace contract), with
+ * the kept tiles recomputed instead of copied:
+ *   vals[k][h][i][c] = exp(s_h[I*B+i][J*B+c] - lse[h][I*B+i]) rounded once to
+ *   `dtype` (round to nearest even) for J*B+c <= I*B+i < N, and 0 elsewhere.
+ */
+int mf_topp_select_bsr_qk(const float* mass, const void* Q, const void* K,
+                          const float* scale, const float* lse, int dtype, int H_s,
+                          int H_ks, int N, int d, int B, float p, int32_t* row_ptr,
+                          int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                          int64_t* nnzb_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Workspace bytes mf_retrieve_fused needs for (N, B, H_kv, d, dtype).  The
  * current kernels need none and return 0 for every configuration; the

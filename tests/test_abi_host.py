@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mf.abi_version() == 1
+    assert mf.abi_version() == 2
     for st in range(5):
         assert L.mf_status_string(st)
     assert b"unknown" in L.mf_status_string(99)
@@ -205,3 +205,61 @@ def test_header_documents_every_entry_point():
         assert m, name
         before = src[max(0, m.start() - 1500):m.start()]
         assert before.rstrip().endswith("*/"), f"{name} has no comment block"
+
+
+# ---- compression from Q and K ----------------------------------------------
+
+def _qk_args(**kw):
+    a = dict(Q=FAKE, K=FAKE, dt=2, H_s=32, H_ks=8, N=4096, d=128, B=64, scale=FAKE, lse=FAKE,
+             mass=FAKE, ws=FAKE, ws_bytes=1 << 30, p=0.9, row_ptr=FAKE, col_idx=FAKE, vals=FAKE,
+             cap=10)
+    a.update(kw)
+    return a
+
+
+QK_BAD = [
+    (dict(dt=7), "dtype"), (dict(H_s=0), "H_s"), (dict(H_s=65), "H_s"), (dict(N=0), "N must"),
+    (dict(H_ks=0), "H_ks"), (dict(H_ks=3), "H_ks"), (dict(d=96), "d must"),
+    (dict(Q=None), "null"), (dict(K=None), "null"), (dict(scale=None), "null"),
+]
+
+
+@pytest.mark.parametrize("kw,frag", QK_BAD)
+def test_row_lse_rejects(L, kw, frag):
+    a = _qk_args(**kw)
+    st = L.mf_row_lse(a["Q"], a["K"], a["dt"], a["H_s"], a["H_ks"], a["N"], a["d"], a["scale"],
+                      a["lse"], None)
+    assert st == mf.MF_ERR_INVALID
+    assert frag in L.mf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,frag", QK_BAD + [(dict(B=48), "B must"), (dict(lse=None), "null"),
+                                              (dict(ws=None), "null"), (dict(ws_bytes=16), "workspace")])
+def test_block_mass_qk_rejects(L, kw, frag):
+    a = _qk_args(**kw)
+    st = L.mf_block_mass_qk(a["Q"], a["K"], a["scale"], a["lse"], a["dt"], a["H_s"], a["H_ks"],
+                            a["N"], a["d"], a["B"], a["mass"], a["ws"], a["ws_bytes"], None)
+    assert st == mf.MF_ERR_INVALID
+    assert frag in L.mf_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,st,frag", [(k, mf.MF_ERR_INVALID, f) for k, f in QK_BAD] + [
+    (dict(p=0.0), mf.MF_ERR_INVALID, "p must"), (dict(p=float("nan")), mf.MF_ERR_INVALID, "p must"),
+    (dict(cap=-1), mf.MF_ERR_INVALID, "cap_nnzb"), (dict(vals=None), mf.MF_ERR_INVALID, "null"),
+    (dict(ws_bytes=4), mf.MF_ERR_INVALID, "workspace"),
+    (dict(N=16 * 4097, B=16), mf.MF_ERR_UNSUPPORTED, "4096")])
+def test_topp_qk_rejects(L, kw, st, frag):
+    a = _qk_args(**kw)
+    r = L.mf_topp_select_bsr_qk(a["mass"], a["Q"], a["K"], a["scale"], a["lse"], a["dt"], a["H_s"],
+                                a["H_ks"], a["N"], a["d"], a["B"], a["p"], a["row_ptr"], a["col_idx"],
+                                a["vals"], a["cap"], None, a["ws"], a["ws_bytes"], None)
+    assert r == st
+    assert frag in L.mf_last_error().decode()
+
+
+def test_block_mass_qk_workspace_size(L):
+    # H_s * ceil(N/16) * T float32 partial sums
+    assert L.mf_block_mass_qk_workspace_bytes(32, 4096, 64) == 32 * 256 * 64 * 4
+    assert L.mf_block_mass_qk_workspace_bytes(3, 100, 32) == 3 * 7 * 4 * 4
+    assert L.mf_block_mass_qk_workspace_bytes(0, 100, 32) == 0
+    assert L.mf_block_mass_qk_workspace_bytes(3, 100, 48) == 0
