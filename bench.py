@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work for the oracle leg")
+    ap.add_argument("--no-qk", action="store_true",
+                    help="skip the compression-without-dense-map leg")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference "
                          "kernel for scaling hardware byte counters)")
@@ -231,9 +233,78 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_qk:
+        out["compress_without_dense_map"] = qk_leg(dev, args.steps)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_leg(w, layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def qk_leg(dev, reps):
+    """Compression from Q and K without a dense map, on the 8B->3B-like pair's
+    first layer (N = 4096, B = 64, H_s = 32, d = 128, fp16, p = 0.95; Q, K from
+    the workload's seeded recipe), timed with HIP events next to the dense
+    path (block mass + selection/gather over the [H_s][N][N] map built from the
+    same Q and K)."""
+    import torch
+    import cross_model_sparse_amd as mf
+    import synth
+    w = synth.workload("pair8b3b-f16")
+    N, B, H_s, d, p = w.N, w.B, w.H_s, w.d, w.p
+    A, Q, K, tau = synth.gen_maps(w, synth.layer_seed(w, 0), device=dev, return_qk=True)
+    Qd = Q.to(device=dev, dtype=torch.float16)
+    Kd = K.to(device=dev, dtype=torch.float16)
+    scale = (1.0 / (d ** 0.5 * tau)).to(device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, reps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    lse = mf.row_lse(Qd, Kd, scale)
+    ws = torch.empty(mf.block_mass_qk_workspace_bytes(H_s, N, B), dtype=torch.uint8, device=dev)
+    mass = mf.block_mass_qk(Qd, Kd, scale, lse, B, workspace=ws)
+    rp, ci, vals, nnzb = mf.topp_select_bsr_qk(mass, Qd, Kd, scale, lse, B, p)
+    wsel = torch.empty(mf.topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev)
+    t_lse = timed(lambda: mf.row_lse(Qd, Kd, scale, out=lse))
+    t_mass = timed(lambda: mf.block_mass_qk(Qd, Kd, scale, lse, B, out=mass, workspace=ws))
+    t_sel = timed(lambda: mf.topp_select_bsr_qk(mass, Qd, Kd, scale, lse, B, p, cap_nnzb=nnzb,
+                                                row_ptr=rp, col_idx=ci, vals=vals,
+                                                workspace=wsel, sync=False))
+    dmass = mf.block_mass(A, B)
+    drp, dci, dvals, dnnzb = mf.topp_select_bsr(dmass, A, B, p)
+    t_dmass = timed(lambda: mf.block_mass(A, B, out=dmass))
+    t_dsel = timed(lambda: mf.topp_select_bsr(dmass, A, B, p, cap_nnzb=dnnzb, row_ptr=drp,
+                                              col_idx=dci, vals=dvals, workspace=wsel,
+                                              sync=False))
+    # one score pass covers the causal pairs (diagonal 32 x 32 tiles computed whole)
+    tiles = sum(i + 1 for i in range(-(-N // 32)))
+    pass_flops = 2.0 * H_s * tiles * 32 * 32 * d
+    gather_flops = 2.0 * nnzb * H_s * B * B * d
+    causal_pairs = N * (N + 1) / 2
+    total = t_lse + t_mass + t_sel
+    return {
+        "workload": f"pair8b3b-f16 layer 0: N={N}, B={B}, H_s={H_s}, K heads {K.shape[0]}, d={d}, fp16, p={p}",
+        "ms": {"row_lse": t_lse, "block_mass_qk": t_mass, "topp_select_bsr_qk": t_sel, "total": total},
+        "dense_path_ms": {"block_mass": t_dmass, "topp_select_bsr": t_dsel,
+                          "total": t_dmass + t_dsel},
+        "dense_map_bytes_not_formed": H_s * N * N * 2,
+        "nnzb": nnzb, "nnzb_dense_path": dnnzb,
+        "mfma_tflops": {"row_lse": pass_flops / t_lse / 1e9, "block_mass_qk": pass_flops / t_mass / 1e9,
+                        "topp_select_bsr_qk": gather_flops / t_sel / 1e9},
+        "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+        "exp_per_s": {"row_lse": H_s * causal_pairs / t_lse * 1e3,
+                      "block_mass_qk": H_s * causal_pairs / t_mass * 1e3},
+    }
 
 
 def cpu_leg(w, layers, budget_s):

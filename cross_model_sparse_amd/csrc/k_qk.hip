@@ -183,8 +183,8 @@ struct KTile {
 
 // Shared walk of lse and mass: a workgroup owns 256 query rows of head h
 // (wavefront w: rows q0 = R0 + 32w .. +31); K tiles of 32 keys are staged
-// through LDS (double-buffered: every thread loads 16 bytes of the next tile
-// into registers while the current one is in use).  body(kt, c) receives the
+// through LDS (two buffers; every thread holds 16 bytes of each of the next
+// two tiles in registers while the current one is in use).  body(kt, c) receives the
 // tile's fp32 scores (in log2 units) for each wavefront whose rows reach key
 // tile kt; mask(...) tells which entries are real.
 template <bool kBF16, int D, class Body>
@@ -219,13 +219,19 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
     const int kr = pc / kRowU4, ch = pc % kRowU4;
     *reinterpret_cast<u32x4*>(smem + buf * KTile<D>::kBytes + kr * KTile<D>::kRowBytes + 16 * ch) = v;
   };
-  u32x4 stage;                                  // D = 128: 512 pieces, one per thread
+  // two tiles in flight in registers: tile kt+1 (stored into LDS after the
+  // compute of tile kt) and tile kt+2 (loaded now), so a tile's load has a
+  // whole iteration to land
+  u32x4 stage_a = {}, stage_b = {};             // D = 128: 512 pieces, one per thread
   const bool has_piece = tid < npieces;
-  if (has_piece) store_piece(0, tid, load_piece(0, tid));
+  if (has_piece) {
+    store_piece(0, tid, load_piece(0, tid));
+    if (nkt > 1) stage_a = load_piece(1, tid);
+  }
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt && has_piece) stage = load_piece(kt + 1, tid);
+    if (kt + 2 < nkt && has_piece) stage_b = load_piece(kt + 2, tid);
     if (kt * 32 <= q0 + 31 && q0 < N) {         // some key of the tile is causal for these rows
       const unsigned char* kb = smem + buf * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
       f32x16 c = {};
@@ -237,11 +243,18 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
       body(kt, c);
     }
     if (kt + 1 < nkt) {
-      if (has_piece) store_piece(buf ^ 1, tid, stage);
+      if (has_piece) store_piece(buf ^ 1, tid, stage_a);
+      stage_a = stage_b;
       __syncthreads();
     }
   }
 }
+
+// 2^x with the hardware instruction alone: results below 2^-126 may flush to
+// zero, which is harmless inside a sum of terms that include a 1 (log-sum-exp),
+// in probabilities compared at 1e-5 relative (block mass) and in stored tile
+// values (an absolute error below 2^-126)
+__device__ __forceinline__ float exp2_sum(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // key of output element e of this lane within a tile
 __device__ __forceinline__ int tile_key(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
@@ -274,9 +287,9 @@ __global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
       }
     }
     if (mx > -INFINITY) {
-      float s = l * exp2f(m - mx);
+      float s = l * exp2_sum(m - mx);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += exp2f(x[e] - mx);
+      for (int e = 0; e < 16; ++e) s += exp2_sum(x[e] - mx);
       l = s;
       m = mx;
     }
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
   const float m2 = __shfl_xor(m, 32);
   const float l2 = __shfl_xor(l, 32);
   const float mm = fmaxf(m, m2);
-  const float ll = (m > -INFINITY ? l * exp2f(m - mm) : 0.f) + (m2 > -INFINITY ? l2 * exp2f(m2 - mm) : 0.f);
+  const float ll = (m > -INFINITY ? l * exp2_sum(m - mm) : 0.f) + (m2 > -INFINITY ? l2 * exp2_sum(m2 - mm) : 0.f);
   if (lane < 32 && row < N) lse[(int64_t)h * N + row] = (mm + log2f(ll)) * kLn2;
 }
 
@@ -322,12 +335,12 @@ __global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
   qk_walk<kBF16, D>(Q, K, h, g, N, R0, scale[h] * kLog2e, smem, [&](int kt, const f32x16& c) {
     if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc += exp2f(c[e] - l2);
+      for (int e = 0; e < 16; ++e) acc += exp2_sum(c[e] - l2);
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = kt * 32 + tile_key(lane, e);
-        acc += (j <= row && j < N && row < N) ? exp2f(c[e] - l2) : 0.f;
+        acc += (j <= row && j < N && row < N) ? exp2_sum(c[e] - l2) : 0.f;
       }
     }
     const int J = kt / tpb;
@@ -336,20 +349,23 @@ __global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
   });
 }
 
-// one wavefront per (kept block, head); per (32-row, 32-key) sub-tile
-template <bool kBF16, int D>
+// one wavefront per (kept block, head).  The block's NSUB = B/32 key
+// sub-tiles are loaded once; for each 32-row sub-tile the NSUB score tiles
+// are independent MFMA chains (their latencies overlap), then exponentiated,
+// rounded and stored, 8 bytes (4 keys) per lane and tile row.
+template <bool kBF16, int D, int NSUB>
 __global__ __launch_bounds__(256) void k_gather_qk_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
-    int H_ks, int N, int B, const float* __restrict__ scale, const float* __restrict__ lse,
+    int H_ks, int N, const float* __restrict__ scale, const float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ kept, int64_t cap,
     int32_t* __restrict__ col_idx, unsigned short* __restrict__ vals) {
   constexpr int NKS = D / 16;
+  constexpr int B = 32 * NSUB;
   const int T = (N + B - 1) / B;
   const int64_t nnzb = row_ptr[T];
   if (nnzb > cap) return;
   const int G = H_s / H_ks;
   const int lane = threadIdx.x & 63;
-  const int nsub = B / 32;
   const int64_t items = nnzb * H_s;
   for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < items; u += (int64_t)gridDim.x * 4) {
     const int64_t k = u / H_s;
@@ -358,28 +374,34 @@ __global__ __launch_bounds__(256) void k_gather_qk_mfma(
     const int J = kept[(int64_t)I * T + (k - row_ptr[I])];
     if (h == 0 && lane == 0) col_idx[k] = J;
     const float sc = scale[h] * kLog2e;
-    const unsigned short* kbase = K + (int64_t)(h / G) * N * D;
     unsigned short* tile = vals + (k * H_s + h) * (int64_t)B * B;
-    for (int qs = 0; qs < nsub; ++qs) {
+    // A operands: key rows J*B + 32 ks + l%32 (clamped), head-dim chunks 8(l/32) + 16 s
+    u32x4 kop[NSUB][NKS];
+#pragma unroll
+    for (int ks = 0; ks < NSUB; ++ks) {
+      const unsigned short* kr = K + ((int64_t)(h / G) * N + min(J * B + ks * 32 + (lane & 31), N - 1)) * D + 8 * (lane >> 5);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) kop[ks][s] = *reinterpret_cast<const u32x4*>(kr + 16 * s);
+    }
+    for (int qs = 0; qs < NSUB; ++qs) {
       const int row = I * B + qs * 32 + (lane & 31);
       const bool row_ok = row < N;
       u32x4 qop[NKS];
-      {
-        const unsigned short* qr = Q + ((int64_t)h * N + min(row, N - 1)) * D + 8 * (lane >> 5);
+      const unsigned short* qr = Q + ((int64_t)h * N + min(row, N - 1)) * D + 8 * (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
-      }
+      for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
       const float l2 = row_ok ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
-      for (int ks = 0; ks < nsub; ++ks) {
-        const int key0 = J * B + ks * 32;
-        f32x16 c = {};
-        if (key0 <= I * B + qs * 32 + 31) {     // not entirely above the diagonal
-          const unsigned short* kr = kbase + (int64_t)min(key0 + (lane & 31), N - 1) * D + 8 * (lane >> 5);
+      f32x16 c[NSUB];
 #pragma unroll
-          for (int s = 0; s < NKS; ++s)
-            c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kr + 16 * s), qop[s], c);
-        }
-        // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4
+      for (int ks = 0; ks < NSUB; ++ks) c[ks] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+#pragma unroll
+        for (int ks = 0; ks < NSUB; ++ks) c[ks] = mfma32<kBF16>(kop[ks][s], qop[s], c[ks]);
+      // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4
+#pragma unroll
+      for (int ks = 0; ks < NSUB; ++ks) {
+        const int key0 = J * B + ks * 32;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           unsigned short hv[4];
@@ -387,8 +409,8 @@ __global__ __launch_bounds__(256) void k_gather_qk_mfma(
           for (int t = 0; t < 4; ++t) {
             const int e = 4 * e4 + t;
             const int j = key0 + tile_key(lane, e);
-            const float v = (row_ok && j <= row) ? exp2f(c[e] * sc - l2) : 0.f;
-            hv[t] = kBF16 ? f32_to_bf16(v) : f32_to_f16(v);
+            const float v = (row_ok && j <= row) ? exp2_sum(c[ks][e] * sc - l2) : 0.f;
+            hv[t] = kBF16 ? __builtin_bit_cast(unsigned short, (__bf16)v) : f32_to_f16(v);
           }
           const int col = ks * 32 + 8 * e4 + 4 * (lane >> 5);
           *reinterpret_cast<u32x2*>(tile + (int64_t)(qs * 32 + (lane & 31)) * B + col) =
@@ -473,8 +495,15 @@ hipError_t gather_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, i
   auto q = reinterpret_cast<const unsigned short*>(Q);
   auto k = reinterpret_cast<const unsigned short*>(K);
   auto v = reinterpret_cast<unsigned short*>(vals);
-  if (d == 128) hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, 128>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, B, scale, lse, row_ptr, kept, cap, col_idx, v);
-  else hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, 64>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, B, scale, lse, row_ptr, kept, cap, col_idx, v);
+#define MF_GQ(D_, NS_) \
+  hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, D_, NS_>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, \
+                     scale, lse, row_ptr, kept, cap, col_idx, v)
+  if (d == 128) {
+    if (B == 32) MF_GQ(128, 1); else if (B == 64) MF_GQ(128, 2); else MF_GQ(128, 4);
+  } else {
+    if (B == 32) MF_GQ(64, 1); else if (B == 64) MF_GQ(64, 2); else MF_GQ(64, 4);
+  }
+#undef MF_GQ
   return hipGetLastError();
 }
 

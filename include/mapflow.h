@@ -174,7 +174,8 @@ int mf_block_mass_qk(const void* Q, const void* K, const float* scale, const flo
  * same row_ptr / col_idx / capacity / nnzb_out / workspace contract), with
  * the kept tiles recomputed instead of copied:
  *   vals[k][h][i][c] = exp(s_h[I*B+i][J*B+c] - lse[h][I*B+i]) rounded once to
- *   `dtype` (round to nearest even) for J*B+c <= I*B+i < N, and 0 elsewhere.
+ *   `dtype` (round to nearest even) for J*B+c <= I*B+i < N, and 0 elsewhere;
+ *   values below 2^-126 may be stored as 0.
  */
 int mf_topp_select_bsr_qk(const float* mass, const void* Q, const void* K,
                           const float* scale, const float* lse, int dtype, int H_s,

@@ -5,7 +5,8 @@ upcasts the same host values exactly.  Bars (derived from the arithmetic, see
 the design notes):
   lse     |gpu - ref| <= N * 2^-24 + 1e-5        (fp32 online sum of <= N terms)
   mass    relative (16 B) * 2^-24 + 1e-5          (fp32 partial of <= 16 B positive terms)
-  tiles   |gpu - ref| <= (half ulp of dtype + 1e-5) |ref| (+ 2^-25 for fp16 subnormals)
+  tiles   |gpu - ref| <= (half ulp of dtype + 1e-5) |ref| + 2^-25 (fp16 subnormals)
+          or 2^-126 (values below it may be stored as 0)
   O       the retrieval bars of tests/_compare.py
 The mass and tile checks feed the oracle's lse (rounded to fp32) to both sides,
 so each step is checked on its own; the end-to-end check runs the product
@@ -107,7 +108,8 @@ def test_qk_compression_parity(name, cfg):
         for t, J in enumerate(kept_ref[I]):
             ref = oracle.bsr_tile(A_ref, B, I, int(J))
             got = vals_h[rp_h[I] + t]
-            bound = (HALF_ULP[dt] + 1e-5) * np.abs(ref) + (2.0 ** -25 if dt == "f16" else 0.0)
+            # + fp16 subnormal spacing; values below 2^-126 may be stored as 0
+            bound = (HALF_ULP[dt] + 1e-5) * np.abs(ref) + (2.0 ** -25 if dt == "f16" else 2.0 ** -126)
             bad = np.abs(got - ref) > bound
             assert not bad.any(), f"row {I} block {J}: {int(bad.sum())} tile entries out of bound"
     assert ties <= max(1, T // 10), f"{ties} tied rows"
