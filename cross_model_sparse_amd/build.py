@@ -30,9 +30,17 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source additions.  The Q/K score kernels consume MFMA results with
+# vector ALU code right away: results in ordinary VGPRs save a copy out of the
+# accumulation registers for every score tile.
+EXTRA_FLAGS = {
+    "k_qk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: Path) -> Path:
     obj = OBJ_DIR / (src.stem + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src.name, []), "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{r.stderr}")

@@ -22,6 +22,8 @@
 // other case (fp32, d = 64/128 with B = 16).
 #include "mf_internal.h"
 
+#include <type_traits>
+
 namespace {
 
 using namespace mfd;
@@ -103,22 +105,29 @@ __global__ __launch_bounds__(256) void k_mass_qk_plain(
   }
 }
 
-// mass[I][J] = (1/H_s) sum_h sum_{tiles of I} part, fp64 in a fixed order
+// mass[I][J] = (1/H_s) sum_h sum_{tiles of I} part, fp64 in a fixed order.
+// Workgroup (I, 64-column chunk); thread (c = t % 64, q = t / 64) adds, for
+// column J = 64 chunk + c, heads q, q+4, q+8, ... and every 16-row tile of
+// block row I in (head, tile) order; the four partial sums are then added in
+// the order q = 0, 1, 2, 3.  The result depends on nothing but the inputs.
 __global__ __launch_bounds__(256) void k_mass_reduce(const float* __restrict__ part, int H_s,
                                                      int N, int B, float* __restrict__ mass) {
+  __shared__ double red[4][64];
   const int T = (N + B - 1) / B;
   const int NRT = (N + kRT - 1) / kRT;
   const int I = blockIdx.x;
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int J = blockIdx.y * 64 + c;
   const int rt0 = I * (B / kRT), rt1 = min(NRT, (I + 1) * (B / kRT));
-  for (int J = threadIdx.x; J < T; J += 256) {
-    float out = 0.f;
-    if (J <= I) {
-      double s = 0.0;
-      for (int h = 0; h < H_s; ++h)
-        for (int rt = rt0; rt < rt1; ++rt) s += (double)part[((int64_t)h * NRT + rt) * T + J];
-      out = (float)(s / (double)H_s);
-    }
-    mass[(int64_t)I * T + J] = out;
+  double s = 0.0;
+  if (J <= I && J < T)
+    for (int h = q; h < H_s; h += 4)
+      for (int rt = rt0; rt < rt1; ++rt) s += (double)part[((int64_t)h * NRT + rt) * T + J];
+  red[q][c] = s;
+  __syncthreads();
+  if (q == 0 && J < T) {
+    const double t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    mass[(int64_t)I * T + J] = J <= I ? (float)(t / (double)H_s) : 0.f;
   }
 }
 
@@ -169,9 +178,10 @@ __global__ __launch_bounds__(256) void k_gather_qk_plain(
 // matrix-core kernels
 // ---------------------------------------------------------------------------
 
-constexpr int kQkWaves = 8;                     // wavefronts per workgroup
-constexpr int kQkThreads = 64 * kQkWaves;
-constexpr int kQkRows = 32 * kQkWaves;          // query rows per workgroup
+constexpr int kQkHalfWaves = 4;                 // wavefronts per half workgroup
+constexpr int kQkHalf = 64 * kQkHalfWaves;      // threads per half
+constexpr int kQkThreads = 2 * kQkHalf;
+constexpr int kQkRows = 32 * kQkHalfWaves;      // query rows per workgroup
 
 // LDS K tile: 32 key rows of D elements, each row padded by 16 bytes so that
 // 16-byte reads of 16 consecutive rows hit distinct banks.
@@ -181,23 +191,32 @@ struct KTile {
   static constexpr int kBytes = 32 * kRowBytes;
 };
 
-// Shared walk of lse and mass: a workgroup owns 256 query rows of head h
-// (wavefront w: rows q0 = R0 + 32w .. +31); K tiles of 32 keys are staged
-// through LDS (two buffers; every thread holds 16 bytes of each of the next
-// two tiles in registers while the current one is in use).  body(kt, c) receives the
-// tile's fp32 scores (in log2 units) for each wavefront whose rows reach key
-// tile kt; mask(...) tells which entries are real.
+// Shared walk of lse and mass over one group of kQkRows query rows of head h.
+// The workgroup's two halves take the same rows (wavefront w of a half: rows
+// q0 = R0 + 32w .. +31) and split the causal key tiles: half 0 walks tiles
+// [0, nfirst), half 1 tiles [nfirst, nkt), with nfirst a multiple of `align`,
+// so the longest walk is half as long.  K tiles of 32 keys are staged through
+// LDS (two buffers per half; every thread holds its pieces of the next two
+// tiles in registers while the current one is in use).  body(kt, c) receives
+// the tile's raw fp32 products q.k for each wavefront whose rows reach key
+// tile kt; the caller multiplies by the scale (in log2 units).  Workgroups are
+// small enough that several share a CU, at different points of their walks,
+// so one's exponentials overlap another's matrix work.
 template <bool kBF16, int D, class Body>
 __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
                                         const unsigned short* __restrict__ K, int h, int g,
-                                        int N, int R0, float sc, unsigned char* smem,
+                                        int N, int R0, int align, unsigned char* smem,
                                         Body&& body) {
   constexpr int NKS = D / 16;                   // MFMA K steps
   constexpr int kRowU4 = D / 8;                 // 16-byte pieces per row
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int q0 = R0 + 32 * wave;
+  constexpr int NP = 32 * kRowU4 / kQkHalf;     // pieces of a tile per thread
+  static_assert(NP * kQkHalf == 32 * kRowU4, "tile pieces must divide evenly");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hf = wave / kQkHalfWaves;           // half of the workgroup
+  const int ht = threadIdx.x % kQkHalf;         // thread within the half
+  const int q0 = R0 + 32 * (wave % kQkHalfWaves);
+  unsigned char* hs = smem + hf * 2 * KTile<D>::kBytes;
   // B operand: this lane's query row (clamped), head-dim chunks 8(l/32) + 16s
   u32x4 qop[NKS];
   {
@@ -208,45 +227,71 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
   }
   const int last_row = min(N, R0 + kQkRows) - 1;
   const int nkt = last_row / 32 + 1;            // key tiles 0..nkt-1
-  // tile loader: 32 rows x D elements = 32 * kRowU4 pieces of 16 bytes
-  const int npieces = 32 * kRowU4;
-  auto load_piece = [&](int kt, int pc) -> u32x4 {
-    const int kr = pc / kRowU4, ch = pc % kRowU4;
-    const int key = min(kt * 32 + kr, N - 1);
-    return *reinterpret_cast<const u32x4*>(K + ((int64_t)g * N + key) * D + 8 * ch);
+  const int nfirst = min(nkt, ((nkt + 1) / 2 + align - 1) / align * align);
+  const int t0 = hf ? nfirst : 0;
+  const int cnt = hf ? nkt - nfirst : nfirst;   // tiles of this half
+  const int nit = nfirst;                       // steps of both halves (nfirst >= nkt - nfirst)
+  // piece pc = ht + kQkHalf * n: key row pc / kRowU4, 16-byte chunk pc % kRowU4;
+  // per-thread offsets are fixed, the tile base is uniform
+  const unsigned short* Kg = K + (int64_t)g * N * D;
+  auto load_tile = [&](int kt, u32x4* v) {
+    if (kt * 32 + 31 < N) {
+      const unsigned short* base = Kg + (int64_t)kt * 32 * D;
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        const int pc = ht + kQkHalf * n;
+        v[n] = *reinterpret_cast<const u32x4*>(base + (pc / kRowU4) * D + 8 * (pc % kRowU4));
+      }
+    } else {                                     // last, partial tile: clamp the key row
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        const int pc = ht + kQkHalf * n;
+        const int key = min(kt * 32 + pc / kRowU4, N - 1);
+        v[n] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * D + 8 * (pc % kRowU4));
+      }
+    }
   };
-  auto store_piece = [&](int buf, int pc, const u32x4& v) {
-    const int kr = pc / kRowU4, ch = pc % kRowU4;
-    *reinterpret_cast<u32x4*>(smem + buf * KTile<D>::kBytes + kr * KTile<D>::kRowBytes + 16 * ch) = v;
+  auto store_tile = [&](int buf, const u32x4* v) {
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      const int pc = ht + kQkHalf * n;
+      *reinterpret_cast<u32x4*>(hs + buf * KTile<D>::kBytes + (pc / kRowU4) * KTile<D>::kRowBytes +
+                                16 * (pc % kRowU4)) = v[n];
+    }
   };
-  // two tiles in flight in registers: tile kt+1 (stored into LDS after the
-  // compute of tile kt) and tile kt+2 (loaded now), so a tile's load has a
-  // whole iteration to land
-  u32x4 stage_a = {}, stage_b = {};             // D = 128: 512 pieces, one per thread
-  const bool has_piece = tid < npieces;
-  if (has_piece) {
-    store_piece(0, tid, load_piece(0, tid));
-    if (nkt > 1) stage_a = load_piece(1, tid);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 2 < nkt && has_piece) stage_b = load_piece(kt + 2, tid);
-    if (kt * 32 <= q0 + 31 && q0 < N) {         // some key of the tile is causal for these rows
-      const unsigned char* kb = smem + buf * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
+  // tile to load for step it of this half (any valid tile once the half is done)
+  auto tile_at = [&](int it) { return min(t0 + min(it, max(cnt - 1, 0)), nkt - 1); };
+  // step it: tile t0+it is in LDS buffer BUF, sa holds the next tile (stored
+  // into the other buffer after the compute), the one after is loaded into sb,
+  // so a tile's load has a whole step to land.  Loads are issued on every step
+  // so that the wait before the LDS store counts only the older tile's loads.
+  // Steps alternate the two register sets and buffers: nothing is copied and
+  // LDS offsets are fixed.  Both halves take the same number of barriers.
+  auto step = [&](auto bufc, int it, u32x4* sa, u32x4* sb) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int kt = t0 + it;
+    load_tile(tile_at(it + 2), sb);
+    if (it < cnt && kt * 32 <= q0 + 31 && q0 < N) {   // some key of the tile is causal for these rows
+      const unsigned char* kb = hs + BUF * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
       f32x16 c = {};
 #pragma unroll
       for (int s = 0; s < NKS; ++s)
         c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kb + 32 * s), qop[s], c);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) c[e] *= sc;
       body(kt, c);
     }
-    if (kt + 1 < nkt) {
-      if (has_piece) store_piece(buf ^ 1, tid, stage_a);
-      stage_a = stage_b;
+    if (it + 1 < nit) {
+      store_tile(BUF ^ 1, sa);
       __syncthreads();
     }
+  };
+  u32x4 stage_a[NP], stage_b[NP];
+  load_tile(tile_at(0), stage_a);
+  store_tile(0, stage_a);
+  load_tile(tile_at(1), stage_a);
+  __syncthreads();
+  for (int it = 0; it < nit; it += 2) {
+    step(std::integral_constant<int, 0>{}, it, stage_a, stage_b);
+    if (it + 1 < nit) step(std::integral_constant<int, 1>{}, it + 1, stage_b, stage_a);
   }
 }
 
@@ -256,6 +301,16 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
 // values (an absolute error below 2^-126)
 __device__ __forceinline__ float exp2_sum(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Work item of a workgroup of the lse / mass kernels: row group grp of head
+// h.  The longest groups (most causal key tiles) of every head come first, so
+// the workgroups that share a CU mix long and short walks; workgroups with
+// equal b mod 8 (one XCD) take the same heads and share their K rows in L2.
+__device__ __forceinline__ void qk_item(int ngrp, int H_s, int& h, int& grp) {
+  const int b = blockIdx.x;
+  h = b % H_s;
+  grp = ngrp - 1 - b / H_s;
+}
+
 // key of output element e of this lane within a tile
 __device__ __forceinline__ int tile_key(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 
@@ -263,43 +318,70 @@ template <bool kBF16, int D>
 __global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
     int H_ks, int N, const float* __restrict__ scale, float* __restrict__ lse) {
-  __shared__ __align__(16) unsigned char smem[2 * KTile<D>::kBytes];
+  __shared__ __align__(16) unsigned char smem[4 * KTile<D>::kBytes];
+  __shared__ float2 half1[kQkRows];              // (max, sum) of half 1 per row
   const int ngrp = (N + kQkRows - 1) / kQkRows;
-  const int h = blockIdx.x / ngrp;
-  const int R0 = (ngrp - 1 - blockIdx.x % ngrp) * kQkRows;   // longest rows first
+  int h, grp;
+  qk_item(ngrp, H_s, h, grp);
   const int g = h / (H_s / H_ks);
+  const float sc = scale[h] * kLog2e;
   const int lane = threadIdx.x & 63;
-  const int q0 = R0 + 32 * (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int R0 = grp * kQkRows;
+  const int q0 = R0 + 32 * (wave % kQkHalfWaves);
   const int row = q0 + (lane & 31);
-  float m = -INFINITY, l = 0.f;
-  qk_walk<kBF16, D>(Q, K, h, g, N, R0, scale[h] * kLog2e, smem, [&](int kt, const f32x16& c) {
-    float x[16];
-    float mx = m;
+  float m = -INFINITY, l = 0.f;                  // running maximum and sum, log2 units
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, 1, smem, [&](int kt, const f32x16& c) {
     if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
+      // the maximum of sc * c is sc times the maximum (sc >= 0) or minimum of c
+      float r = c[0];
+      if (sc >= 0.f) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { x[e] = c[e]; mx = fmaxf(mx, x[e]); }
+        for (int e = 1; e < 16; ++e) r = fmaxf(r, c[e]);
+      } else {
+#pragma unroll
+        for (int e = 1; e < 16; ++e) r = fminf(r, c[e]);
+      }
+      const float mx = fmaxf(m, r * sc);
+      float s = l * exp2_sum(m - mx);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += exp2_sum(fmaf(c[e], sc, -mx));
+      l = s;
+      m = mx;
     } else {
+      float x[16];
+      float mx = m;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = kt * 32 + tile_key(lane, e);
-        x[e] = (j <= row && j < N) ? c[e] : -INFINITY;
+        x[e] = (j <= row && j < N) ? c[e] * sc : -INFINITY;
         mx = fmaxf(mx, x[e]);
       }
-    }
-    if (mx > -INFINITY) {
-      float s = l * exp2_sum(m - mx);
+      if (mx > -INFINITY) {
+        float s = l * exp2_sum(m - mx);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += exp2_sum(x[e] - mx);
-      l = s;
-      m = mx;
+        for (int e = 0; e < 16; ++e) s += exp2_sum(x[e] - mx);
+        l = s;
+        m = mx;
+      }
     }
   });
-  // lanes l and l+32 hold the same row: merge their (max, sum)
-  const float m2 = __shfl_xor(m, 32);
-  const float l2 = __shfl_xor(l, 32);
-  const float mm = fmaxf(m, m2);
-  const float ll = (m > -INFINITY ? l * exp2_sum(m - mm) : 0.f) + (m2 > -INFINITY ? l2 * exp2_sum(m2 - mm) : 0.f);
-  if (lane < 32 && row < N) lse[(int64_t)h * N + row] = (mm + log2f(ll)) * kLn2;
+  // merge (max, sum) pairs: lanes l and l+32 of a wavefront hold the same row,
+  // then the two halves (half 0 merges in half 1's pair)
+  auto merge = [](float& m, float& l, float m2, float l2) {
+    const float mm = fmaxf(m, m2);
+    l = (m > -INFINITY ? l * exp2_sum(m - mm) : 0.f) + (m2 > -INFINITY ? l2 * exp2_sum(m2 - mm) : 0.f);
+    m = mm;
+  };
+  merge(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
+  const int r = row - R0;
+  if (wave >= kQkHalfWaves && lane < 32) half1[r] = make_float2(m, l);
+  __syncthreads();
+  if (wave < kQkHalfWaves && lane < 32 && row < N) {
+    const float2 o = half1[r];
+    merge(m, l, o.x, o.y);
+    lse[(int64_t)h * N + row] = (m + log2f(l)) * kLn2;
+  }
 }
 
 template <bool kBF16, int D>
@@ -307,46 +389,61 @@ __global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
     int H_ks, int N, int B, const float* __restrict__ scale, const float* __restrict__ lse,
     float* __restrict__ part) {
-  __shared__ __align__(16) unsigned char smem[2 * KTile<D>::kBytes];
+  __shared__ __align__(16) unsigned char smem[4 * KTile<D>::kBytes];
   const int T = (N + B - 1) / B;
   const int NRT = (N + kRT - 1) / kRT;
   const int ngrp = (N + kQkRows - 1) / kQkRows;
-  const int h = blockIdx.x / ngrp;
-  const int R0 = (ngrp - 1 - blockIdx.x % ngrp) * kQkRows;
+  int h, grp;
+  qk_item(ngrp, H_s, h, grp);
   const int g = h / (H_s / H_ks);
+  const float sc = scale[h] * kLog2e;
   const int lane = threadIdx.x & 63;
-  const int q0 = R0 + 32 * (threadIdx.x >> 6);
-  const int row = q0 + (lane & 31);
-  const float l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
   const int tpb = B / 32;                        // key tiles per column block
-  float acc = 0.f;
-  // sums of the lanes of one 16-row tile: lanes {0..15, 32..47} and {16..31, 48..63}
-  auto flush = [&](int J) {
-    float v = acc;
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 32);
-    const int rt = q0 / kRT + ((lane >> 4) & 1);
-    if ((lane == 0 || lane == 16) && rt * kRT < N) part[((int64_t)h * NRT + rt) * T + J] = v;
-    acc = 0.f;
-  };
-  qk_walk<kBF16, D>(Q, K, h, g, N, R0, scale[h] * kLog2e, smem, [&](int kt, const f32x16& c) {
-    if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
+  {
+    const int R0 = grp * kQkRows;
+    const int q0 = R0 + 32 * ((threadIdx.x >> 6) % kQkHalfWaves);
+    const int row = q0 + (lane & 31);
+    const float l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
+    float acc = 0.f;
+    // sums of the lanes of one 16-row tile: lanes {0..15, 32..47} and {16..31, 48..63}
+    auto flush = [&](int J) {
+      float v = acc;
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 32);
+      const int rt = q0 / kRT + ((lane >> 4) & 1);
+      if ((lane == 0 || lane == 16) && rt * kRT < N) part[((int64_t)h * NRT + rt) * T + J] = v;
+      acc = 0.f;
+    };
+    // halves split at a column-block boundary: each block's partials come from one half
+    qk_walk<kBF16, D>(Q, K, h, g, N, R0, tpb, smem, [&](int kt, const f32x16& c) {
+      if (kt * 32 + 31 <= q0 && q0 + 31 < N) {  // every key of the tile is causal for every row
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc += exp2_sum(c[e] - l2);
-    } else {
+        for (int e = 0; e < 16; ++e) acc += exp2_sum(fmaf(c[e], sc, -l2));
+      } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = kt * 32 + tile_key(lane, e);
-        acc += (j <= row && j < N && row < N) ? exp2_sum(c[e] - l2) : 0.f;
+        for (int e = 0; e < 16; ++e) {
+          const int j = kt * 32 + tile_key(lane, e);
+          acc += (j <= row && j < N && row < N) ? exp2_sum(fmaf(c[e], sc, -l2)) : 0.f;
+        }
       }
-    }
-    const int J = kt / tpb;
-    // the block's last tile, or the last tile these rows reach
-    if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) flush(J);
-  });
+      const int J = kt / tpb;
+      // the block's last tile, or the last tile these rows reach
+      if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) flush(J);
+    });
+  }
+}
+
+// two values rounded to the storage type (RNE), packed low first
+template <bool kBF16>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  if constexpr (kBF16)
+    return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a) |
+           ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+  else
+    return (unsigned)f32_to_f16(a) | ((unsigned)f32_to_f16(b) << 16);
 }
 
 // one wavefront per (kept block, head).  The block's NSUB = B/32 key
@@ -390,7 +487,8 @@ __global__ __launch_bounds__(256) void k_gather_qk_mfma(
       const unsigned short* qr = Q + ((int64_t)h * N + min(row, N - 1)) * D + 8 * (lane >> 5);
 #pragma unroll
       for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
-      const float l2 = row_ok ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
+      // rows past N: an infinite shift makes every value exactly 0
+      const float l2 = row_ok ? lse[(int64_t)h * N + row] * kLog2e : INFINITY;
       f32x16 c[NSUB];
 #pragma unroll
       for (int ks = 0; ks < NSUB; ++ks) c[ks] = f32x16{};
@@ -398,26 +496,156 @@ __global__ __launch_bounds__(256) void k_gather_qk_mfma(
       for (int s = 0; s < NKS; ++s)
 #pragma unroll
         for (int ks = 0; ks < NSUB; ++ks) c[ks] = mfma32<kBF16>(kop[ks][s], qop[s], c[ks]);
-      // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4
+      // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4.
+      // Below the diagonal block every key is causal for every row.
+      const bool diag = J == I;
 #pragma unroll
       for (int ks = 0; ks < NSUB; ++ks) {
         const int key0 = J * B + ks * 32;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          unsigned short hv[4];
+          float v[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int e = 4 * e4 + t;
-            const int j = key0 + tile_key(lane, e);
-            const float v = (row_ok && j <= row) ? exp2_sum(c[ks][e] * sc - l2) : 0.f;
-            hv[t] = kBF16 ? __builtin_bit_cast(unsigned short, (__bf16)v) : f32_to_f16(v);
+            v[t] = exp2_sum(fmaf(c[ks][e], sc, -l2));
+            if (diag && key0 + tile_key(lane, e) > row) v[t] = 0.f;
           }
           const int col = ks * 32 + 8 * e4 + 4 * (lane >> 5);
           *reinterpret_cast<u32x2*>(tile + (int64_t)(qs * 32 + (lane & 31)) * B + col) =
-              u32x2{(unsigned)hv[0] | ((unsigned)hv[1] << 16), (unsigned)hv[2] | ((unsigned)hv[3] << 16)};
+              u32x2{pack2<kBF16>(v[0], v[1]), pack2<kBF16>(v[2], v[3])};
         }
       }
     }
+  }
+}
+
+// Kept tiles for B = 64 and 128: a workgroup of four wavefronts takes up to
+// kGC consecutive kept blocks (in BSR order, so mostly of one block row) of
+// one head.  The query operand of each wavefront (32 rows of the block row)
+// stays in registers while the row does not change.  Per block, the K block
+// (B contiguous rows) comes into LDS through coalesced 16-byte loads issued
+// one block ahead; each wavefront computes NSUB*NSUB/4 score sub-tiles of
+// 32 x 32, exponentiates and rounds them into an LDS copy of the output tile;
+// the tile (B*B contiguous elements) then leaves with coalesced 16-byte
+// stores.  Workgroup (x, y): head x (the heads that one XCD serves share
+// their Q and K rows in its L2), block group y, y + gridDim.y, ...
+constexpr int kGC = 8;                           // kept blocks per block group
+
+template <bool kBF16, int D, int NSUB>
+__global__ __launch_bounds__(256) void k_gather_qk_rows(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
+    int H_ks, int N, const float* __restrict__ scale, const float* __restrict__ lse,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ kept, int64_t cap,
+    int32_t* __restrict__ col_idx, unsigned short* __restrict__ vals) {
+  constexpr int B = 32 * NSUB;
+  constexpr int NKS = D / 16;                    // MFMA K steps
+  constexpr int kRowU4 = D / 8;                  // 16-byte pieces per K row
+  constexpr int KROW = D * 2 + 16;               // LDS bytes per K row (padded)
+  constexpr int OROW = B * 2 + 16;               // LDS bytes per output row (padded)
+  constexpr int NPK = B * kRowU4 / 256;          // K pieces per thread
+  constexpr int kOutU4 = B / 8;                  // 16-byte pieces per output row
+  constexpr int NPO = B * kOutU4 / 256;          // output pieces per thread
+  constexpr int KPW = NSUB * NSUB / 4;           // score sub-tiles per wavefront
+  static_assert(NPK * 256 == B * kRowU4 && NPO * 256 == B * kOutU4, "pieces must divide evenly");
+  __shared__ __align__(16) unsigned char k_lds[B * KROW];
+  __shared__ __align__(16) unsigned char o_lds[B * OROW];
+  const int T = (N + B - 1) / B;
+  const int64_t nnzb = row_ptr[T];
+  if (nnzb > cap) return;
+  const int h = blockIdx.x;
+  const int g = h / (H_s / H_ks);
+  const float sc = scale[h] * kLog2e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qs = wave * KPW / NSUB;              // this wavefront's 32-row sub-tile
+  const unsigned short* Kg = K + (int64_t)g * N * D;
+  // K block J: uniform base and fixed per-thread offsets; only the last,
+  // partial block clamps its key rows
+  auto load_k = [&](int J, u32x4* v) {
+    if (J * B + B <= N) {
+      const unsigned short* base = Kg + (int64_t)J * B * D;
+#pragma unroll
+      for (int n = 0; n < NPK; ++n) {
+        const int pc = tid + 256 * n;
+        v[n] = *reinterpret_cast<const u32x4*>(base + (pc / kRowU4) * D + 8 * (pc % kRowU4));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NPK; ++n) {
+        const int pc = tid + 256 * n;
+        const int key = min(J * B + pc / kRowU4, N - 1);
+        v[n] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * D + 8 * (pc % kRowU4));
+      }
+    }
+  };
+  for (int64_t k0 = (int64_t)blockIdx.y * kGC; k0 < nnzb; k0 += (int64_t)gridDim.y * kGC) {
+    const int64_t k1 = min(nnzb, k0 + kGC);
+    int I = row_of(row_ptr, T, k0);
+    int In = I;                                  // row of the prefetched block
+    int Iq = -1;                                 // row whose queries are in qop
+    u32x4 qop[NKS];
+    float l2 = 0.f;
+    u32x4 kst[NPK];
+    load_k(kept[(int64_t)I * T + (k0 - row_ptr[I])], kst);
+    for (int64_t k = k0; k < k1; ++k) {
+      I = In;
+      const int J = kept[(int64_t)I * T + (k - row_ptr[I])];
+      if (h == 0 && tid == 0) col_idx[k] = J;
+      // K block of k into LDS, then the next block's loads
+#pragma unroll
+      for (int n = 0; n < NPK; ++n) {
+        const int pc = tid + 256 * n;
+        *reinterpret_cast<u32x4*>(k_lds + (pc / kRowU4) * KROW + 16 * (pc % kRowU4)) = kst[n];
+      }
+      if (k + 1 < k1) {
+        while (row_ptr[In + 1] <= k + 1) ++In;
+        load_k(kept[(int64_t)In * T + (k + 1 - row_ptr[In])], kst);
+      }
+      const int row = I * B + qs * 32 + (lane & 31);
+      if (I != Iq) {                             // B operand: query rows of this row block
+        const unsigned short* qr = Q + ((int64_t)h * N + min(row, N - 1)) * D + 8 * (lane >> 5);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+        // rows past N: an infinite shift makes every value exactly 0
+        l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : INFINITY;
+        Iq = I;
+      }
+      __syncthreads();                           // K block in LDS; the previous tile has left
+      // lane: row qs*32 + l%32 of the tile, keys ks*32 + 8(e/4) + 4(l/32) + e%4.
+      // Below the diagonal block every key is causal for every row.
+      const bool diag = J == I;
+#pragma unroll
+      for (int i = 0; i < KPW; ++i) {
+        const int ks = (wave * KPW + i) % NSUB;
+        const unsigned char* kb = k_lds + (ks * 32 + (lane & 31)) * KROW + 16 * (lane >> 5);
+        f32x16 c = {};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+          c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kb + 32 * s), qop[s], c);
+        const int key0 = J * B + ks * 32;
+        unsigned char* ob = o_lds + (qs * 32 + (lane & 31)) * OROW + 2 * (ks * 32 + 4 * (lane >> 5));
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int e = 4 * e4 + t;
+            v[t] = exp2_sum(fmaf(c[e], sc, -l2));
+            if (diag && key0 + tile_key(lane, e) > row) v[t] = 0.f;
+          }
+          *reinterpret_cast<u32x2*>(ob + 16 * e4) = u32x2{pack2<kBF16>(v[0], v[1]), pack2<kBF16>(v[2], v[3])};
+        }
+      }
+      __syncthreads();                           // output tile complete in LDS
+      unsigned short* tile = vals + (k * H_s + h) * (int64_t)B * B;
+#pragma unroll
+      for (int n = 0; n < NPO; ++n) {
+        const int pc = tid + 256 * n;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(o_lds + (pc / kOutU4) * OROW + 16 * (pc % kOutU4));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(tile + (pc / kOutU4) * B + 8 * (pc % kOutU4)));
+      }
+    }
+    __syncthreads();                             // LDS is reused by the next block group
   }
 }
 
@@ -498,12 +726,26 @@ hipError_t gather_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, i
 #define MF_GQ(D_, NS_) \
   hipLaunchKernelGGL((k_gather_qk_mfma<kBF16, D_, NS_>), grid, dim3(256), 0, st, q, k, H_s, H_ks, N, \
                      scale, lse, row_ptr, kept, cap, col_idx, v)
-  if (d == 128) {
-    if (B == 32) MF_GQ(128, 1); else if (B == 64) MF_GQ(128, 2); else MF_GQ(128, 4);
-  } else {
-    if (B == 32) MF_GQ(64, 1); else if (B == 64) MF_GQ(64, 2); else MF_GQ(64, 4);
-  }
+  if (B == 32 || (reinterpret_cast<uintptr_t>(vals) & 15) != 0) {   // per-wavefront tiles, 8-byte stores
+    if (d == 128) {
+      if (B == 32) MF_GQ(128, 1); else if (B == 64) MF_GQ(128, 2); else MF_GQ(128, 4);
+    } else {
+      if (B == 32) MF_GQ(64, 1); else if (B == 64) MF_GQ(64, 2); else MF_GQ(64, 4);
+    }
 #undef MF_GQ
+    return hipGetLastError();
+  }
+  const int64_t groups = (std::min<int64_t>(cap, (int64_t)T * (T + 1) / 2) + kGC - 1) / kGC;
+  const dim3 grid_rows(H_s, (unsigned)std::min<int64_t>(groups, 65535));
+#define MF_GR(D_, NS_) \
+  hipLaunchKernelGGL((k_gather_qk_rows<kBF16, D_, NS_>), grid_rows, dim3(256), 0, st, q, k, H_s, H_ks, \
+                     N, scale, lse, row_ptr, kept, cap, col_idx, v)
+  if (d == 128) {
+    if (B == 64) MF_GR(128, 2); else MF_GR(128, 4);
+  } else {
+    if (B == 64) MF_GR(64, 2); else MF_GR(64, 4);
+  }
+#undef MF_GR
   return hipGetLastError();
 }
 
@@ -537,7 +779,8 @@ hipError_t launch_block_mass_qk(const void* Q, const void* K, const float* scale
   else if (dt == MF_F16) e = mass_plain<mfd::TF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
   else e = mass_plain<mfd::TBF16>(Q, K, H_s, H_ks, N, d, B, scale, lse, part, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_mass_reduce, dim3(blocks_of(N, B)), dim3(256), 0, st, part, H_s, N, B, mass);
+  hipLaunchKernelGGL(k_mass_reduce, dim3(blocks_of(N, B), (blocks_of(N, B) + 63) / 64), dim3(256), 0,
+                     st, part, H_s, N, B, mass);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 """Short text summaries of rocprofv3 output for the profiles/ folder.
 
-    python -m cross_model_sparse_amd.profile_summary stats STATS_CSV --command CMD
+    python -m cross_model_sparse_amd.profile_summary stats STATS_CSV --command CMD [--match TEXT ...]
         per-kernel call count and average / total duration from a
-        `rocprofv3 --kernel-trace --stats` run (run_kernel_stats.csv)
+        `rocprofv3 --kernel-trace --stats` run (run_kernel_stats.csv),
+        optionally only for kernels whose names contain one of the TEXTs
 
     python -m cross_model_sparse_amd.profile_summary traffic \\
         --fetch FETCH_CSV --write WRITE_CSV --copy-mib M --kernel NAME \\
@@ -31,8 +32,10 @@ def _short(name: str, n: int = 90) -> str:
     return name if len(name) <= n else name[: n - 3] + "..."
 
 
-def stats(path: str, command: str, top: int = 12) -> str:
+def stats(path: str, command: str, top: int = 12, match=None) -> str:
     rows = list(csv.DictReader(open(path)))
+    if match:
+        rows = [r for r in rows if any(m in r["Name"] for m in match)]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"# rocprofv3 --kernel-trace --stats summary", f"command: {command}", "",
            f"{'calls':>6} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
@@ -113,6 +116,8 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--match", action="append",
+                   help="keep only kernels whose name contains this text (repeatable)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -122,7 +127,7 @@ def main(argv=None):
     t.add_argument("--write-command", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        sys.stdout.write(stats(a.csv, a.command, a.top))
+        sys.stdout.write(stats(a.csv, a.command, a.top, a.match))
     else:
         sys.stdout.write(traffic(a.fetch, a.write, a.copy_mib, a.kernel, a.fetch_command,
                                  a.write_command))
