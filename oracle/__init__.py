@@ -22,7 +22,10 @@ article on it, aitest123.com/news/zaoi86), step by step in the pages' order:
    (article, third component; paper page, highlight 4);
 5. the same compression computed from the sender's Q and K and the per-row
    log-sum-exp of its scores, without a dense map (article, third section,
-   first component).
+   first component);
+6. retrieval over a packed batch of sequences (paper page, "Practical
+   Implementation Details": the serving integration runs under chunked prefill
+   and paged caches), each sequence on its own.
 
 Readings of points the pages leave open (the head-map formula in highlight 2 is
 garbled; the statistic, stop rule, tie order, GQA grouping and padding are not
@@ -38,10 +41,12 @@ than itself: dense causal attention from torch's scaled_dot_product_attention,
 brute-force dense decompress-then-matmul, scipy.sparse BSR products, exhaustive
 subset search for the Top-p rule, closed-form block-mass identities, a
 hand-worked example, and for the Q/K compression torch's causal softmax and
-logsumexp, the all-zero-score closed form and plain-loop brute force.  No function here is "parity unpinned".
+logsumexp, the all-zero-score closed form and plain-loop brute force, and for
+the packed batch dense causal attention of each sequence (torch) and a
+per-token brute force.  No function here is "parity unpinned".
 """
 from .mapflow_ref import (  # noqa: F401
     n_blocks, block_mass_row, block_mass, topp_row, decision_masses, topp_select,
     bsr_tile, build_bsr, retrieve_row, retrieve, compress, pipeline_row,
-    row_lse, QKMap, compress_qk,
+    row_lse, QKMap, compress_qk, retrieve_varlen,
 )

@@ -306,3 +306,41 @@ def compress_qk(Q, K, scale, B: int, p: float, lse=None):
     A = QKMap(Q, K, scale, lse)
     mass, kept, row_ptr, col_idx, vals = compress(A, B, p)
     return lse, mass, kept, row_ptr, col_idx, vals
+
+
+# ---------------------------------------------------------------------------
+# 6. retrieval over a packed batch of sequences
+# ---------------------------------------------------------------------------
+
+# The pages' serving integration runs under chunked prefill and paged KV caches
+# (paper page, "Practical Implementation Details").  A packed batch carries S
+# sequences back to back: sequence s holds tokens cu_seqlens[s] ..
+# cu_seqlens[s+1]-1 of V and O and block rows cu_rows[s] .. cu_rows[s+1]-1 of a
+# row_ptr that numbers the rows of all sequences in turn; col_idx is local to
+# each sequence; kept block k's tiles sit in page block_table[k] of a pool
+# (page k without a table).  Each sequence is retrieved on its own: nothing
+# crosses a sequence boundary.
+
+def retrieve_varlen(cu_seqlens, cu_rows, row_ptr, col_idx, pool, W, V, B: int,
+                    block_table=None) -> np.ndarray:
+    """O[total][H_r][d] fp64: retrieve() for every sequence of a packed batch."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cr = np.asarray(cu_rows, dtype=np.int64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col_idx = np.asarray(col_idx, dtype=np.int64)
+    V = np.asarray(V)
+    H_r = np.asarray(W).shape[0]
+    O = np.zeros((V.shape[0], H_r, V.shape[2]), dtype=F64)
+    for s in range(len(cu) - 1):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        g0, g1 = int(cr[s]), int(cr[s + 1])
+        N = t1 - t0
+        if N == 0:
+            continue
+        assert g1 - g0 == n_blocks(N, B)
+        k0, k1 = int(row_ptr[g0]), int(row_ptr[g1])
+        ks = np.arange(k0, k1)
+        pages = ks if block_table is None else np.asarray(block_table, dtype=np.int64)[ks]
+        O[t0:t1] = retrieve(row_ptr[g0:g1 + 1] - k0, col_idx[k0:k1], np.asarray(pool)[pages],
+                            W, V[t0:t1], N, B)
+    return O

@@ -470,3 +470,132 @@ def test_qk_planted_mistakes_are_detected():
                 lse_with(lambda h: h // 2, use_scale=False)):
         with pytest.raises(AssertionError):
             np.testing.assert_allclose(bad, lse_ref, rtol=0, atol=1e-6)
+
+
+# ---- packed batches: retrieve_varlen -----------------------------------------
+
+def _pack(seqs, B, rng, shuffle=True):
+    """Pack per-sequence BSR states (row_ptr, col_idx, vals) into one batch with
+    the pool pages in a random order; returns the batch arrays and the table."""
+    cu, cr, rp, ci, tiles = [0], [0], [0], [], []
+    for (N, row_ptr, col_idx, vals) in seqs:
+        cu.append(cu[-1] + N)
+        cr.append(cr[-1] + len(row_ptr) - 1)
+        base = rp[-1]
+        rp.extend(int(x) + base for x in row_ptr[1:])
+        ci.extend(int(x) for x in col_idx)
+        tiles.extend(vals)
+    nnzb = len(ci)
+    perm = rng.permutation(nnzb) if shuffle else np.arange(nnzb)
+    pool = np.zeros((nnzb,) + np.asarray(tiles[0]).shape)
+    for k in range(nnzb):
+        pool[perm[k]] = tiles[k]
+    return np.array(cu), np.array(cr), np.array(rp), np.array(ci), pool, perm
+
+
+def test_varlen_identity_reproduces_each_sequence_attention():
+    # p = 1, W = I: every sequence of the batch is its own dense causal attention
+    rng = np.random.default_rng(31)
+    B, H, d = 16, 3, 8
+    lens = [1, 40, 16, 73]
+    seqs, refs, Vs = [], [], []
+    for n in lens:
+        q = torch.from_numpy(rng.standard_normal((H, n, d)))
+        k = torch.from_numpy(rng.standard_normal((H, n, d)))
+        v = rng.standard_normal((n, H, d))
+        A = torch.softmax((q @ k.transpose(1, 2)) / math.sqrt(d) +
+                          torch.triu(torch.full((n, n), -math.inf, dtype=torch.float64), 1), -1).numpy()
+        _, _, rp, ci, vals = oracle.compress(A, B, 1.0)
+        seqs.append((n, rp, ci, vals))
+        vt = torch.from_numpy(v).permute(1, 0, 2).contiguous()
+        refs.append(torch.nn.functional.scaled_dot_product_attention(q, k, vt, is_causal=True)
+                    .permute(1, 0, 2).numpy())
+        Vs.append(v)
+    cu, cr, rp, ci, pool, table = _pack(seqs, B, rng)
+    O = oracle.retrieve_varlen(cu, cr, rp, ci, pool, np.eye(H), np.concatenate(Vs), B, table)
+    ref = np.concatenate(refs)
+    assert np.abs(O - ref).max() < 1e-12 * np.abs(ref).max()
+
+
+def _varlen_brute(cu, cr, rp, ci, pool, W, V, B, table):
+    """Token by token: O[t][r] = sum over the kept blocks of t's block row of
+    sum_c (sum_s W[r][s] tile[s][i][c]) V[first token + J*B + c][r/G]."""
+    H_r, d = W.shape[0], V.shape[2]
+    G = H_r // V.shape[1]
+    O = np.zeros((V.shape[0], H_r, d))
+    for s in range(len(cu) - 1):
+        for t in range(cu[s], cu[s + 1]):
+            loc = t - cu[s]
+            g = cr[s] + loc // B
+            i = loc % B
+            for k in range(rp[g], rp[g + 1]):
+                J = ci[k]
+                tile = pool[table[k]]
+                for c in range(B):
+                    key = J * B + c
+                    if key >= cu[s + 1] - cu[s]:
+                        continue
+                    for r in range(H_r):
+                        a = sum(W[r, h] * tile[h, i, c] for h in range(tile.shape[0]))
+                        O[t, r] += a * V[cu[s] + key, r // G]
+    return O
+
+
+def test_varlen_matches_token_by_token_brute_force():
+    rng = np.random.default_rng(32)
+    B, H_s, H_r, H_kv, d = 8, 2, 4, 2, 3
+    lens = [5, 17, 8, 0, 12]
+    seqs = []
+    for n in lens:
+        if n == 0:
+            seqs.append((0, np.array([0]), np.array([], dtype=np.int64), np.zeros((0, H_s, B, B))))
+            continue
+        A = _random_causal_map(rng, H_s, n)
+        _, _, rp, ci, vals = oracle.compress(A, B, 0.7)
+        seqs.append((n, rp, ci, vals))
+    tiles = [v for s in seqs for v in s[3]]
+    cu, cr, rp, ci, _, _ = _pack([s for s in seqs if s[0]], B, rng, shuffle=False)
+    # rebuild with the empty sequence kept in place
+    cu = np.cumsum([0] + lens)
+    cr = np.cumsum([0] + [oracle.n_blocks(n, B) if n else 0 for n in lens])
+    perm = rng.permutation(len(tiles))
+    pool = np.zeros((len(tiles), H_s, B, B))
+    for k, t in enumerate(tiles):
+        pool[perm[k]] = t
+    W = rng.standard_normal((H_r, H_s))
+    V = rng.standard_normal((cu[-1], H_kv, d))
+    O = oracle.retrieve_varlen(cu, cr, rp, ci, pool, W, V, B, perm)
+    ref = _varlen_brute(cu, cr, rp, ci, pool, W, V, B, perm)
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+
+
+def test_varlen_planted_mistakes_are_detected():
+    # the brute force above rejects: ignoring the block table, global instead of
+    # local columns, and a sequence's V taken from the start of the batch
+    rng = np.random.default_rng(33)
+    B, H_s, H_r, H_kv, d = 8, 2, 2, 1, 4
+    lens = [9, 20]
+    seqs = []
+    for n in lens:
+        A = _random_causal_map(rng, H_s, n)
+        _, _, rp, ci, vals = oracle.compress(A, B, 0.9)
+        seqs.append((n, rp, ci, vals))
+    cu, cr, rp, ci, pool, table = _pack(seqs, B, rng)
+    W = rng.standard_normal((H_r, H_s))
+    V = rng.standard_normal((cu[-1], H_kv, d))
+    ref = _varlen_brute(cu, cr, rp, ci, pool, W, V, B, table)
+    good = oracle.retrieve_varlen(cu, cr, rp, ci, pool, W, V, B, table)
+    np.testing.assert_allclose(good, ref, atol=1e-12)
+    bad_table = oracle.retrieve_varlen(cu, cr, rp, ci, pool, W, V, B, None)
+    ci_global = ci.copy()
+    for s in range(len(lens)):
+        k0, k1 = rp[cr[s]], rp[cr[s + 1]]
+        ci_global[k0:k1] += cr[s]
+    # global columns point past the second sequence's own blocks: clamp so the
+    # oracle still runs, which must change the result
+    bad_cols = oracle.retrieve_varlen(cu, cr, rp, np.minimum(ci_global, 2), pool, W, V, B, table)
+    V_shift = V.copy()
+    V_shift[cu[1]:] = V[:cu[-1] - cu[1]]
+    bad_v = oracle.retrieve_varlen(cu, cr, rp, ci, pool, W, V_shift, B, table)
+    for bad in (bad_table, bad_cols, bad_v):
+        assert np.abs(bad - ref).max() > 1e-6
