@@ -15,7 +15,7 @@ retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
 bounded sample of block rows of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
-                    [--copy-ref-mib M]
+                    [--no-qk] [--no-varlen] [--copy-ref-mib M]
 """
 from __future__ import annotations
 
@@ -43,6 +43,8 @@ def parse():
                     help="target CPU work for the oracle leg")
     ap.add_argument("--no-qk", action="store_true",
                     help="skip the compression-without-dense-map leg")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed-batch (varlen) retrieval leg")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference "
                          "kernel for scaling hardware byte counters)")
@@ -235,6 +237,8 @@ def main():
 
     if not args.no_qk:
         out["compress_without_dense_map"] = qk_leg(dev, args.steps)
+    if not args.no_varlen:
+        out["varlen_batch"] = varlen_leg(dev, max(5, args.steps))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_leg(w, layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -304,6 +308,103 @@ def qk_leg(dev, reps):
         "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
         "exp_per_s": {"row_lse": H_s * causal_pairs / t_lse * 1e3,
                       "block_mass_qk": H_s * causal_pairs / t_mass * 1e3},
+    }
+
+
+def varlen_leg(dev, reps):
+    """The packed varlen batch: 16 sequences, lengths U[1024, 16384] (seeded),
+    B = 64, H_s = 32, H_r = 24, H_kv = 8, d = 128, bf16, p = 0.9, structured
+    maps.  Each sequence's dense map is generated, compressed (block mass +
+    Top-p/BSR, HIP events) and freed in turn; the kept tiles of all sequences
+    then sit in one pool in a shuffled page order.  Timed with HIP events
+    (medians over `reps`): the whole batch's retrieval in one launch through
+    the block table, the same over a contiguous pool without a table, and one
+    retrieval launch per sequence."""
+    import torch
+    import cross_model_sparse_amd as mf
+    import synth
+    w0 = synth.workload("varlen-bf16")
+    lens = synth.varlen_lengths(w0)
+    B, p, e = w0.B, w0.p, synth.DTYPE_BYTES[w0.dtype]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    seqs, W, t_comp = [], None, 0.0
+    for s, n in enumerate(lens):
+        g = synth.gen_layer(w0.with_(N=n), device=dev, seed=5000 + s)
+        if W is None:
+            W = g["W"].to(dev)
+        A = g["A"]
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        mass = mf.block_mass(A, B)
+        rp, ci, vals, nnzb = mf.topp_select_bsr(mass, A, B, p)   # reads nnzb: one sync
+        b.record(stream)
+        b.synchronize()
+        t_comp += a.elapsed_time(b)
+        seqs.append(dict(N=n, rp=rp, ci=ci[:nnzb], vals=vals[:nnzb].clone(), nnzb=nnzb,
+                         V=g["V"].to(dev)))
+        del A, mass, vals, g
+        torch.cuda.empty_cache()
+    S = len(seqs)
+    Ts = [-(-n // B) for n in lens]
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    cu, cr = i32(np.cumsum([0] + lens).tolist()), i32(np.cumsum([0] + Ts).tolist())
+    offs = np.cumsum([0] + [x["nnzb"] for x in seqs])
+    row_ptr = torch.cat([torch.zeros(1, dtype=torch.int32, device=dev)] +
+                        [x["rp"][1:] + int(o) for x, o in zip(seqs, offs)])
+    col_idx = torch.cat([x["ci"] for x in seqs])
+    contig = torch.cat([x["vals"] for x in seqs])
+    nnzb = int(offs[-1])
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(nnzb)).to(dev)
+    pool = torch.empty_like(contig)
+    pool[perm] = contig
+    table = perm.to(torch.int32)
+    V = torch.cat([x["V"] for x in seqs])
+    O = torch.empty(V.shape[0], w0.H_r, w0.d, dtype=V.dtype, device=dev)
+    Os = [torch.empty(x["N"], w0.H_r, w0.d, dtype=V.dtype, device=dev) for x in seqs]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_tab = timed(lambda: mf.retrieve_fused_varlen(cu, cr, row_ptr, col_idx, pool, nnzb, W, V, B,
+                                                   block_table=table, out=O))
+    t_con = timed(lambda: mf.retrieve_fused_varlen(cu, cr, row_ptr, col_idx, contig, nnzb, W, V, B,
+                                                   out=O))
+
+    def per_seq():
+        for x, o in zip(seqs, Os):
+            mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], W, x["V"], x["N"], B, out=o)
+    t_seq = timed(per_seq)
+    tokens = int(sum(lens))
+    alg = sum(x["nnzb"] * w0.H_s * B * B * e + x["N"] * w0.H_kv * w0.d * e
+              + x["N"] * w0.H_r * w0.d * e + 4 * (T + 1 + x["nnzb"]) for x, T in zip(seqs, Ts))
+    alg += 4 * w0.H_r * w0.H_s + 8 * (S + 1)
+    alg_tab = alg + 4 * nnzb
+    return {
+        "workload": f"varlen-bf16: {S} sequences, lengths U[1024, 16384] (total {tokens} tokens), "
+                    f"B={B}, H_s={w0.H_s}, H_r={w0.H_r}, H_kv={w0.H_kv}, d={w0.d}, bf16, p={p}",
+        "lengths": lens,
+        "nnzb_total": nnzb,
+        "ms": {"one_launch_paged_pool": t_tab, "one_launch_contiguous_pool": t_con,
+               "one_launch_per_sequence": t_seq, "compress_all_sequences": t_comp},
+        "query_tokens_per_s": {"one_launch_paged_pool": tokens / t_tab * 1e3,
+                               "one_launch_contiguous_pool": tokens / t_con * 1e3,
+                               "one_launch_per_sequence": tokens / t_seq * 1e3,
+                               "compress_plus_one_launch": tokens / (t_comp + t_tab) * 1e3},
+        "roofline_one_launch_paged": {"bound": "hbm", "bytes": alg_tab,
+                                      "achieved": alg_tab / t_tab / 1e6, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": alg_tab / t_tab / 1e6 / HBM_PEAK_GBS},
     }
 
 

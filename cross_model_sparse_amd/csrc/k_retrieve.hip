@@ -53,6 +53,17 @@
 // k_retrieve_simple (every other supported case, including fp32)
 //   One workgroup per (block row, receiver head): the mixed tile is built in
 //   LDS in fp32, then multiplied with V by plain fp32 FMAs.
+//
+// Packed batches (chunked prefill and paged caches are what the pages' serving
+// integration has to live with: paper page, "Practical Implementation
+// Details"): both kernels also take a batch of sequences in one launch.  The
+// block rows of all sequences are numbered globally (sequence s owns rows
+// cu_rows[s] .. cu_rows[s+1]-1 of row_ptr) and V, O are packed by token
+// (sequence s starts at token cu_seqlens[s]); a work item finds its sequence
+// by binary search and then runs exactly as for a single sequence.  An
+// optional block table names, for each kept block, its page in a tile pool,
+// so the compressed state of many sequences (or layers) can live in one
+// allocation; a page outside the pool contributes nothing.
 #include <algorithm>
 
 #include "mf_internal.h"
@@ -139,6 +150,55 @@ __device__ __forceinline__ unsigned short bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Packed batches
+// ---------------------------------------------------------------------------
+
+// A packed batch of sequences.  Kernels take it with kVar = true; with kVar =
+// false they see one sequence of N tokens whose block rows are the whole
+// row_ptr, and the batch fields are not read.
+struct Batch {
+  const int32_t* cu_rows;      // [S+1] first global block row of each sequence
+  const int32_t* cu_seqlens;   // [S+1] first token of each sequence in V and O
+  const int32_t* block_table;  // [nnzb] pool page of each kept block, or nullptr
+  int64_t n_pages;             // tiles in the pool (bounds block_table entries)
+  int S;
+};
+
+// The sequence of global block row Ig: its local row I, block rows T, tokens
+// N and first token tok0.  False when the row holds no query row.
+struct RowView {
+  int I, T, N;
+  int64_t tok0;
+};
+template <bool kVar>
+__device__ __forceinline__ bool row_view(const Batch& bt, int Ig, int N, int B, RowView& rv) {
+  if (!kVar) {
+    rv.I = Ig;
+    rv.N = N;
+    rv.T = (N + B - 1) / B;
+    rv.tok0 = 0;
+    return true;
+  }
+  int lo = 0, hi = bt.S - 1;                     // last s with cu_rows[s] <= Ig
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bt.cu_rows[mid] <= Ig) lo = mid; else hi = mid - 1;
+  }
+  rv.I = Ig - bt.cu_rows[lo];
+  rv.T = bt.cu_rows[lo + 1] - bt.cu_rows[lo];
+  rv.tok0 = bt.cu_seqlens[lo];
+  rv.N = bt.cu_seqlens[lo + 1] - bt.cu_seqlens[lo];
+  return rv.I >= 0 && rv.I < rv.T && (int64_t)rv.I * B < rv.N;
+}
+// Pool page of kept block k, or -1 when the table points outside the pool.
+template <bool kVar>
+__device__ __forceinline__ int64_t page_of(const Batch& bt, int64_t k) {
+  if (!kVar || bt.block_table == nullptr) return k;
+  const int64_t p = bt.block_table[k];
+  return (p >= 0 && p < bt.n_pages) ? p : -1;
+}
+
+// ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
 
@@ -187,13 +247,13 @@ struct HmPlan {
 // NPAIR = ceil(RPW / 2) receiver pairs per wavefront, RPW = H_r / 8 receivers
 // (a pair's second receiver past RPW is computed from valid data and never
 // stored).  lg_ncc = log2(B / 16).
-template <bool kBF16, int NCH, int NPAIR>
+template <bool kBF16, int NCH, int NPAIR, bool kVar>
 __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N, int B,
     int lg_ncc, const float* __restrict__ W, int H_r, int RPW, int G,
     const unsigned short* __restrict__ V, int64_t ldV,
-    unsigned short* __restrict__ O, int64_t ldO, int RG) {
+    unsigned short* __restrict__ O, int64_t ldO, int RG, Batch bt, int R) {
   using Plan = HmPlan<kBF16, NCH>;
   constexpr int NBOP = Plan::NBOP;
   constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
@@ -210,10 +270,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   static_assert(NPAIR == 1 || NPAIR == 2, "receiver pairs per wavefront");
   __shared__ __align__(16) unsigned char smem[kSmem];
 
-  const int T = (N + B - 1) / B;
   const int subs = B / kRows;
-  int I, sub;
-  if (!item_of(blockIdx.x, subs, T, RG, &I, &sub)) return;
+  int Ig, sub;                                   // global block row, 16-row slice
+  if (!item_of(blockIdx.x, subs, R, RG, &Ig, &sub)) return;
+  RowView rv;
+  if (!row_view<kVar>(bt, Ig, N, B, rv)) return;
+  const int I = rv.I;                            // block row within its sequence
+  const int T = rv.T;
+  N = rv.N;
+  V += rv.tok0 * ldV;
+  O += rv.tok0 * ldO;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -261,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 
   const int rbeg = wave * RPW;
   const int g = rbeg / G;
-  int64_t kb = row_ptr[I], ke = row_ptr[I + 1];
+  int64_t kb = row_ptr[Ig], ke = row_ptr[Ig + 1];
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
   const int ncc_mask = (1 << lg_ncc) - 1;
@@ -281,6 +347,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     return kb + (t >= cnt ? t - cnt : t);
   };
   auto col_ok = [&](int J) { return J >= 0 && J < T; };
+  // column of chunk x's block; -1 (never valid) when its page is outside the pool
+  auto col_of = [&](int x) -> int {
+    const int64_t k = block_of(x);
+    if constexpr (!kVar) return col_idx[k];
+    else return page_of<kVar>(bt, k) >= 0 ? col_idx[k] : -1;
+  };
 
   // tile-slice copy d of this wavefront: 1 KB piece pr = wave + 8d (heads 2pr,
   // 2pr+1), issued only for pr < NPR, so wavefronts issue NDV or NDV-1 copies;
@@ -299,7 +371,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   // slices of one block row take the block's chunks in staggered order
   auto vals_src = [&](int x) -> const unsigned short* {
     const int xc = x < n_chunks ? x : n_chunks - 1;
-    return vals + block_of(x) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
+    if constexpr (!kVar) return vals + block_of(x) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
+    const int64_t pg = page_of<kVar>(bt, block_of(x));
+    return vals + (pg < 0 ? 0 : pg) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
   };
   auto copy_piece = [&](const unsigned short* src, int slot, int d) {
     if (d < ndv_w) dma16s(head_off[d], src, smem_lds + slot * kStage + (wave + kWaves * d) * 1024);
@@ -508,8 +582,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   int J1 = 0;                                    // column of chunk u+1
   int slot = 0;                                  // u % NSTG
   if (n_chunks > 0) {
-    const int J0 = col_idx[block_of(0)];
-    J1 = col_idx[block_of(1)];
+    const int J0 = col_of(0);
+    J1 = col_of(1);
     issue_v(0, J0);
 #pragma unroll
     for (int st = 0; st < NSTG; ++st) issue_vals(st, st);
@@ -520,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     lds_barrier();
   }
   for (int u = 0; u < n_chunks; ++u) {
-    const int Jn = col_idx[block_of(u + 2)];
+    const int Jn = col_of(u + 2);
     u32x4 vt[4];
     read_vt(vt);
     const unsigned short* vsrc = vals_src(u + NSTG);
@@ -580,18 +654,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 // Plain kernel
 // ---------------------------------------------------------------------------
 
-template <class TT, int BB, int D>
+template <class TT, int BB, int D, bool kVar>
 __global__ __launch_bounds__(kSimpleThreads) void k_retrieve_simple(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const typename TT::S* __restrict__ vals, int64_t nnzb, int H_s, int N,
     const float* __restrict__ W, int H_r, const typename TT::S* __restrict__ V,
-    int H_kv, int64_t ldV, typename TT::S* __restrict__ O, int64_t ldO) {
+    int H_kv, int64_t ldV, typename TT::S* __restrict__ O, int64_t ldO, Batch bt, int R) {
   constexpr int RPP = kSimpleThreads / D;        // query rows per pass
   constexpr int NACC = BB / RPP;           // rows per thread
   __shared__ float ahat[BB * BB];
   __shared__ float wrow[64];
-  const int T = (N + BB - 1) / BB;
-  const int I = T - 1 - (int)blockIdx.x;
+  const int Ig = R - 1 - (int)blockIdx.x;        // global block row, last first
+  RowView rv;
+  if (!row_view<kVar>(bt, Ig, N, BB, rv)) return;
+  const int T = rv.T;
+  const int I = rv.I;
+  N = rv.N;
+  V += rv.tok0 * ldV;
+  O += rv.tok0 * ldO;
   const int r = blockIdx.y;
   const int g = r / (H_r / H_kv);
   const int tid = threadIdx.x;
@@ -601,14 +681,15 @@ __global__ __launch_bounds__(kSimpleThreads) void k_retrieve_simple(
   float acc[NACC];
 #pragma unroll
   for (int m = 0; m < NACC; ++m) acc[m] = 0.f;
-  int64_t kb = row_ptr[I], ke = row_ptr[I + 1];
+  int64_t kb = row_ptr[Ig], ke = row_ptr[Ig + 1];
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
   __syncthreads();
   for (int64_t k = kb; k < ke; ++k) {
     const int J = col_idx[k];
-    if (J < 0 || J >= T) continue;
-    const typename TT::S* blk = vals + k * H_s * BB * BB;
+    const int64_t pg = page_of<kVar>(bt, k);
+    if (J < 0 || J >= T || pg < 0) continue;
+    const typename TT::S* blk = vals + pg * H_s * BB * BB;
     for (int e = tid; e < BB * BB; e += kSimpleThreads) {
       float s = 0.f;
       for (int h = 0; h < H_s; ++h) s += wrow[h] * TT::tof(blk[(int64_t)h * BB * BB + e]);
@@ -634,13 +715,19 @@ template <class TT, int BB, int D>
 int launch_simple_t(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
                     int64_t nnzb, int H_s, int N, const float* W, int H_r,
                     const void* V, int H_kv, int64_t ldV, void* O, int64_t ldO,
-                    hipStream_t st) {
+                    const Batch& bt, int R, hipStream_t st) {
   using S = typename TT::S;
-  const int T = mf::blocks_of(N, BB);
-  hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D>), dim3(T, H_r), dim3(kSimpleThreads),
-                     0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
-                     nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
-                     ldV, reinterpret_cast<S*>(O), ldO);
+  if (R <= 0) return MF_OK;
+  if (bt.cu_rows)
+    hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D, true>), dim3(R, H_r), dim3(kSimpleThreads),
+                       0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
+                       nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
+                       ldV, reinterpret_cast<S*>(O), ldO, bt, R);
+  else
+    hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D, false>), dim3(R, H_r), dim3(kSimpleThreads),
+                       0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
+                       nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
+                       ldV, reinterpret_cast<S*>(O), ldO, bt, R);
   return mf::hip_check(hipGetLastError(), "k_retrieve_simple launch");
 }
 
@@ -648,12 +735,12 @@ template <class TT, int D>
 int launch_simple_d(int B, const int32_t* row_ptr, const int32_t* col_idx,
                     const void* vals, int64_t nnzb, int H_s, int N, const float* W,
                     int H_r, const void* V, int H_kv, int64_t ldV, void* O,
-                    int64_t ldO, hipStream_t st) {
+                    int64_t ldO, const Batch& bt, int R, hipStream_t st) {
   switch (B) {
-    case 16: return launch_simple_t<TT, 16, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
-    case 32: return launch_simple_t<TT, 32, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
-    case 64: return launch_simple_t<TT, 64, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
-    default: return launch_simple_t<TT, 128, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
+    case 16: return launch_simple_t<TT, 16, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+    case 32: return launch_simple_t<TT, 32, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+    case 64: return launch_simple_t<TT, 64, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+    default: return launch_simple_t<TT, 128, D>(row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
   }
 }
 
@@ -661,10 +748,10 @@ template <class TT>
 int launch_simple(int B, int d, const int32_t* row_ptr, const int32_t* col_idx,
                   const void* vals, int64_t nnzb, int H_s, int N, const float* W,
                   int H_r, const void* V, int H_kv, int64_t ldV, void* O,
-                  int64_t ldO, hipStream_t st) {
+                  int64_t ldO, const Batch& bt, int R, hipStream_t st) {
   if (d == 64)
-    return launch_simple_d<TT, 64>(B, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
-  return launch_simple_d<TT, 128>(B, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
+    return launch_simple_d<TT, 64>(B, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+  return launch_simple_d<TT, 128>(B, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
 }
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -674,12 +761,17 @@ int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
                   const int32_t* col_idx, const unsigned short* vals, int64_t nnzb,
                   int H_s, int N, int B, int lg_ncc, const float* W, int H_r, int RPW,
                   int G, const unsigned short* V, int64_t ldV, unsigned short* O,
-                  int64_t ldO, int RG) {
-#define MF_CASE(NCH_)                                                                      \
-  case NCH_:                                                                               \
-    hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR>), grid, dim3(kThreads), 0, st, \
-                       row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,    \
-                       V, ldV, O, ldO, RG);                                                \
+                  int64_t ldO, int RG, const Batch& bt, int R) {
+#define MF_CASE(NCH_)                                                                            \
+  case NCH_:                                                                                     \
+    if (bt.cu_rows)                                                                              \
+      hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR, true>), grid, dim3(kThreads), 0, st, \
+                         row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
+                         V, ldV, O, ldO, RG, bt, R);                                             \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR, false>), grid, dim3(kThreads), 0, st, \
+                         row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
+                         V, ldV, O, ldO, RG, bt, R);                                             \
     break;
   switch (NCH) {
     MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5) MF_CASE(6)
@@ -710,15 +802,18 @@ bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const 
 
 size_t retrieve_workspace_bytes(int, int, int, int, int) { return 0; }
 
-int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
-                    const void* vals, int64_t nnzb, int dt, int H_s, int N,
-                    int B, const float* W, int H_r, const void* V, int H_kv,
-                    int d, int64_t ldV, void* O, int64_t ldO, void*, size_t,
-                    hipStream_t st) {
+namespace {
+
+// R block rows (all sequences of bt); N is the single sequence's length when
+// bt.cu_rows is null.
+int retrieve_impl(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                  int64_t nnzb, int dt, int H_s, int N, int B, const float* W, int H_r,
+                  const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                  const Batch& bt, int R, hipStream_t st) {
+  if (R <= 0) return MF_OK;
   if (retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO)) {
-    const int T = blocks_of(N, B);
-    const int RG = std::max(1, T / 16);
-    const int groups = (T + RG - 1) / RG;
+    const int RG = std::max(1, R / 16);
+    const int groups = (R + RG - 1) / RG;
     const int rows_per_xcd = ((groups + 7) / 8) * RG;
     const dim3 grid(rows_per_xcd * 8 * (B / kRows));
     const int NCH = (H_s + 7) / 8;
@@ -729,16 +824,39 @@ int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
     auto Op = reinterpret_cast<unsigned short*>(O);
     const bool bf = dt == MF_BF16;
     if (RPW > 2)
-      return bf ? launch_mfma_p<true, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG)
-                : launch_mfma_p<false, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG);
-    return bf ? launch_mfma_p<true, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG)
-              : launch_mfma_p<false, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG);
+      return bf ? launch_mfma_p<true, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
+                : launch_mfma_p<false, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
+    return bf ? launch_mfma_p<true, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
+              : launch_mfma_p<false, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
   }
   if (dt == MF_F32)
-    return launch_simple<mfd::TF32>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
+    return launch_simple<mfd::TF32>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
   if (dt == MF_F16)
-    return launch_simple<mfd::TF16>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
-  return launch_simple<mfd::TBF16>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, st);
+    return launch_simple<mfd::TF16>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+  return launch_simple<mfd::TBF16>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
+}
+
+}  // namespace
+
+int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
+                    const void* vals, int64_t nnzb, int dt, int H_s, int N,
+                    int B, const float* W, int H_r, const void* V, int H_kv,
+                    int d, int64_t ldV, void* O, int64_t ldO, void*, size_t,
+                    hipStream_t st) {
+  const Batch bt{nullptr, nullptr, nullptr, nnzb, 1};
+  return retrieve_impl(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W, H_r, V, H_kv, d, ldV,
+                       O, ldO, bt, blocks_of(N, B), st);
+}
+
+int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const int32_t* block_table, const void* vals, int64_t n_pages,
+                           int64_t nnzb, int dt, int H_s, int B, const float* W, int H_r,
+                           const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                           hipStream_t st) {
+  const Batch bt{cu_rows, cu_seqlens, block_table, block_table ? n_pages : nnzb, S};
+  return retrieve_impl(row_ptr, col_idx, vals, nnzb, dt, H_s, 0, B, W, H_r, V, H_kv, d, ldV,
+                       O, ldO, bt, R, st);
 }
 
 }  // namespace mf

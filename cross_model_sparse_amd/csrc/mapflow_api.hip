@@ -277,4 +277,27 @@ int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                              (hipStream_t)stream);
 }
 
+int mf_retrieve_fused_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
+                             const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* block_table, const void* vals, int64_t n_pages,
+                             int64_t nnzb, int dtype, int H_s, int B, const float* W, int H_r,
+                             const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                             void* stream) {
+  const char* fn = "mf_retrieve_fused_varlen";
+  if (S < 1) return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": S must be >= 1 (got %lld)", S));
+  if (R < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": R < 0");
+  // N = 1 stands in for the per-sequence lengths, which live on the device
+  const int st = check_retrieve_shape(fn, dtype, H_s, 1, B, H_r, H_kv, d, ldV, ldO);
+  if (st != MF_OK) return st;
+  if (!cu_seqlens || !cu_rows || !row_ptr || !W || !V || !O)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": nnzb < 0");
+  if (nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with nnzb > 0");
+  if (block_table && n_pages < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": n_pages < 0");
+  return mf::launch_retrieve_varlen(S, R, cu_seqlens, cu_rows, row_ptr, col_idx, block_table, vals,
+                                    n_pages, nnzb, dtype, H_s, B, W, H_r, V, H_kv, d, ldV, O, ldO,
+                                    (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -48,6 +48,13 @@ int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     int B, const float* W, int H_r, const void* V, int H_kv,
                     int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
                     size_t workspace_bytes, hipStream_t st);
+// One launch over a packed batch of S sequences (R block rows in total).
+int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           const int32_t* block_table, const void* vals, int64_t n_pages,
+                           int64_t nnzb, int dt, int H_s, int B, const float* W, int H_r,
+                           const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                           hipStream_t st);
 size_t retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dt);
 // True when launch_retrieve runs the matrix-core kernel for these arguments.
 bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const void* vals,

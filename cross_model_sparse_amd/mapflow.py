@@ -25,7 +25,8 @@ _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
-            "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused")
+            "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
+            "mf_retrieve_fused_varlen")
 
 
 class MapflowError(RuntimeError):
@@ -93,6 +94,10 @@ def load() -> ctypes.CDLL:
     L.mf_retrieve_fused.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
                                     c_vp, c_int, c_vp, c_int, c_int, c_i64, c_vp, c_i64,
                                     c_vp, c_sz, c_vp]
+    L.mf_retrieve_fused_varlen.restype = c_int
+    L.mf_retrieve_fused_varlen.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_i64, c_i64, c_int, c_int, c_int, c_vp, c_int,
+                                           c_vp, c_int, c_int, c_i64, c_vp, c_i64, c_vp]
     _lib = L
     return L
 
@@ -241,6 +246,46 @@ def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Ten
                                     _dcode(V), H_s, N, B, _ptr(W), H_r, _ptr(V), H_kv, d,
                                     V.stride(0), _ptr(out), out.stride(0), _ptr(workspace),
                                     ws_bytes, _stream(stream)))
+    return out
+
+
+def retrieve_fused_varlen(cu_seqlens: torch.Tensor, cu_rows: torch.Tensor,
+                          row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                          nnzb: int, W: torch.Tensor, V: torch.Tensor, B: int,
+                          block_table: torch.Tensor | None = None, R: int | None = None,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """O[total][H_r][d] for a packed batch of sequences in one launch
+    (mf_retrieve_fused_varlen).  cu_seqlens / cu_rows are device int32 [S+1];
+    row_ptr covers the R = cu_rows[S] block rows of all sequences; col_idx is
+    local to each sequence; vals is the tile pool [n_pages][H_s][B][B], indexed
+    through block_table when given.  R, when not given, is len(row_ptr) - 1."""
+    _need_cuda(cu_seqlens, cu_rows, row_ptr, col_idx, vals, W, V)
+    for t, name in ((cu_seqlens, "cu_seqlens"), (cu_rows, "cu_rows"), (row_ptr, "row_ptr")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise MapflowError(MF_ERR_INVALID, f"{name} must be a contiguous int32 tensor")
+    if cu_rows.numel() != cu_seqlens.numel():
+        raise MapflowError(MF_ERR_INVALID, "cu_rows and cu_seqlens must both have S+1 entries")
+    S = cu_seqlens.numel() - 1
+    R = row_ptr.numel() - 1 if R is None else int(R)
+    H_s = vals.shape[1]
+    H_r = W.shape[0]
+    if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != H_s:
+        raise MapflowError(MF_ERR_INVALID, "W must be a contiguous fp32 [H_r][H_s] tensor")
+    if V.dim() != 3 or V.stride(2) != 1 or V.stride(1) != V.shape[2]:
+        raise MapflowError(MF_ERR_INVALID, "V must be [total][H_kv][d] with contiguous rows")
+    if V.dtype != vals.dtype:
+        raise MapflowError(MF_ERR_INVALID, "V and vals must share a dtype")
+    if block_table is not None and (block_table.dtype != torch.int32 or not block_table.is_contiguous()):
+        raise MapflowError(MF_ERR_INVALID, "block_table must be a contiguous int32 tensor")
+    H_kv, d = V.shape[1], V.shape[2]
+    if out is None:
+        out = torch.empty(V.shape[0], H_r, d, dtype=V.dtype, device=V.device)
+    if out.dim() != 3 or out.stride(2) != 1 or out.stride(1) != d:
+        raise MapflowError(MF_ERR_INVALID, "out must be [total][H_r][d] with contiguous rows")
+    _check(load().mf_retrieve_fused_varlen(
+        S, R, _ptr(cu_seqlens), _ptr(cu_rows), _ptr(row_ptr), _ptr(col_idx), _ptr(block_table),
+        _ptr(vals), vals.shape[0], int(nnzb), _dcode(V), H_s, B, _ptr(W), H_r, _ptr(V), H_kv, d,
+        V.stride(0), _ptr(out), out.stride(0), _stream(stream)))
     return out
 
 

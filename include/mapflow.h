@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 2
+#define MF_ABI_VERSION 3
 
 typedef enum {
   MF_OK = 0,
@@ -242,6 +242,49 @@ int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                       int N, int B, const float* W, int H_r, const void* V,
                       int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused retrieval over a packed batch of sequences in one launch (the pages'
+ * serving integration runs under chunked prefill and paged KV caches: paper
+ * page, "Practical Implementation Details").  For each sequence s it computes
+ * exactly what mf_retrieve_fused computes for that sequence alone, with the
+ * same kernels and the same arithmetic (outputs are bitwise identical).
+ *
+ *  S           host, number of sequences, >= 1.
+ *  R           host, number of block rows of all sequences (= cu_rows[S]);
+ *              it sizes the grid.
+ *  cu_seqlens  device, [S+1] int32, nondecreasing from 0: sequence s holds
+ *              tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of V and O
+ *              (N_s = cu_seqlens[s+1] - cu_seqlens[s] tokens).
+ *  cu_rows     device, [S+1] int32, nondecreasing from 0: sequence s owns
+ *              global block rows cu_rows[s] .. cu_rows[s+1]-1, with
+ *              cu_rows[s+1] - cu_rows[s] = ceil(N_s / B).
+ *  row_ptr     device, [R+1] int32, monotone from 0: kept blocks of global
+ *              block row g are k = row_ptr[g] .. row_ptr[g+1]-1 (k < nnzb).
+ *  col_idx     device, [nnzb] int32: each kept block's column block, local to
+ *              its sequence (in [0, ceil(N_s/B))).
+ *  block_table device, [nnzb] int32 or NULL: the pool page holding kept block
+ *              k's tiles.  NULL means page k (a contiguous pool).
+ *  vals        device, the tile pool [n_pages][H_s][B][B] of `dtype`
+ *              (n_pages is ignored when block_table is NULL: the pool then
+ *              holds nnzb pages).
+ *  W, V, O     as in mf_retrieve_fused, with V and O packed by token.
+ *  Rows past a sequence's end, columns outside [0, ceil(N_s/B)), pages
+ *  outside [0, n_pages) and indices k outside [0, nnzb) are skipped rather
+ *  than read, so malformed tables cannot make the kernels read outside the
+ *  caller's buffers; the device arrays are not otherwise validated.
+ *  Ownership: the caller owns every buffer; nothing is retained after the call.
+ *  Errors: MF_ERR_INVALID for S < 1, R < 0, nnzb < 0, n_pages < 0 with a
+ *  block table, a null pointer (col_idx and vals may be NULL only when
+ *  nnzb == 0; block_table may be NULL), and the dtype, B, H_s, H_r, H_kv, d
+ *  and stride checks of mf_retrieve_fused.
+ */
+int mf_retrieve_fused_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
+                             const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* block_table, const void* vals, int64_t n_pages,
+                             int64_t nnzb, int dtype, int H_s, int B, const float* W, int H_r,
+                             const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mf.abi_version() == 2
+    assert mf.abi_version() == 3
     for st in range(5):
         assert L.mf_status_string(st)
     assert b"unknown" in L.mf_status_string(99)
@@ -263,3 +263,33 @@ def test_block_mass_qk_workspace_size(L):
     assert L.mf_block_mass_qk_workspace_bytes(3, 100, 32) == 3 * 7 * 4 * 4
     assert L.mf_block_mass_qk_workspace_bytes(0, 100, 32) == 0
     assert L.mf_block_mass_qk_workspace_bytes(3, 100, 48) == 0
+
+
+# ---- packed batches -----------------------------------------------------------
+
+def _varlen(L, **kw):
+    a = dict(S=3, R=10, cu=FAKE, cr=FAKE, row_ptr=FAKE, col_idx=FAKE, table=None, vals=FAKE,
+             n_pages=0, nnzb=5, dt=2, H_s=40, B=64, W=FAKE, H_r=32, V=FAKE, H_kv=8, d=128,
+             ldV=8 * 128, O=FAKE, ldO=32 * 128)
+    a.update(kw)
+    return L.mf_retrieve_fused_varlen(a["S"], a["R"], a["cu"], a["cr"], a["row_ptr"], a["col_idx"],
+                                      a["table"], a["vals"], a["n_pages"], a["nnzb"], a["dt"],
+                                      a["H_s"], a["B"], a["W"], a["H_r"], a["V"], a["H_kv"], a["d"],
+                                      a["ldV"], a["O"], a["ldO"], None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(S=0), "S must"), (dict(R=-1), "R < 0"), (dict(cu=None), "null"), (dict(cr=None), "null"),
+    (dict(row_ptr=None), "null"), (dict(O=None), "null"), (dict(nnzb=-1), "nnzb"),
+    (dict(col_idx=None), "null col_idx/vals"), (dict(table=FAKE, n_pages=-2), "n_pages"),
+    (dict(B=48), "B must"), (dict(H_s=0), "H_s"), (dict(H_r=30), "multiple of H_kv"),
+    (dict(d=96), "d must"), (dict(ldO=100), "ldO"), (dict(dt=5), "dtype"),
+])
+def test_retrieve_varlen_rejects(L, kw, frag):
+    assert _varlen(L, **kw) == mf.MF_ERR_INVALID
+    assert frag in _last(L)
+
+
+def test_retrieve_varlen_empty_batch_launches_nothing(L):
+    # R = 0 block rows: valid, nothing to do (no GPU work is queued)
+    assert _varlen(L, R=0, nnzb=0, col_idx=None, vals=None) == mf.MF_OK

@@ -72,9 +72,10 @@ def test_checker_accepts_the_fixed_forms(tmp_path):
 
 
 # one instantiation per code shape: bf16/fp16, 1 or 2 receiver pairs, 2 or 3
-# tile buffers, the four head-mix plans (full groups, remainder 1, 2, 3)
-KERNELS = ["ILb1ELi5ELi2E", "ILb1ELi6ELi2E", "ILb1ELi3ELi1E", "ILb0ELi4ELi2E",
-           "ILb0ELi6ELi1E", "ILb1ELi1ELi1E"]
+# tile buffers, the four head-mix plans (full groups, remainder 1, 2, 3), each
+# for one sequence (Lb0E) and for a packed batch (Lb1E)
+KERNELS = [k + v for k in ("ILb1ELi5ELi2E", "ILb1ELi6ELi2E", "ILb1ELi3ELi1E", "ILb0ELi4ELi2E",
+                           "ILb0ELi6ELi1E", "ILb1ELi1ELi1E") for v in ("Lb0E", "Lb1E")]
 
 
 @pytest.fixture(scope="module")
