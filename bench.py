@@ -15,7 +15,7 @@ retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
 bounded sample of block rows of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
-                    [--no-qk] [--no-varlen] [--copy-ref-mib M]
+                    [--no-qk] [--no-varlen] [--no-fanout] [--copy-ref-mib M]
 """
 from __future__ import annotations
 
@@ -45,6 +45,8 @@ def parse():
                     help="skip the compression-without-dense-map leg")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-batch (varlen) retrieval leg")
+    ap.add_argument("--no-fanout", action="store_true",
+                    help="skip the one-sender-several-receivers leg")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference "
                          "kernel for scaling hardware byte counters)")
@@ -237,6 +239,8 @@ def main():
 
     if not args.no_qk:
         out["compress_without_dense_map"] = qk_leg(dev, args.steps)
+    if not args.no_fanout:
+        out["fanout"] = fanout_leg(dev, w, layers, max(5, args.steps))
     if not args.no_varlen:
         out["varlen_batch"] = varlen_leg(dev, max(5, args.steps))
     if not args.no_cpu:
@@ -308,6 +312,68 @@ def qk_leg(dev, reps):
         "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
         "exp_per_s": {"row_lse": H_s * causal_pairs / t_lse * 1e3,
                       "block_mass_qk": H_s * causal_pairs / t_mass * 1e3},
+    }
+
+
+def fanout_leg(dev, w, layers, reps):
+    """One sender state feeding two receivers: the BSR states of the step's
+    layers (14B->8B-like sender, N = 8192, B = 64, H_s = 40, bf16) feed the
+    8B-like receiver of the workload (H_r = 32, H_kv = 8) and a second,
+    1.7B-like receiver (H_r = 16, H_kv = 8; W ~ N(0, 1/H_s), V ~ N(0, 1),
+    seeded).  HIP events per layer, medians over `reps` passes over all layers:
+    one joint launch (mf_retrieve_fused_multi) against the two receivers'
+    launches back to back.  Algorithmic bytes of the pair: the kept tiles once,
+    both receivers' V and O, indices and both head maps."""
+    import torch
+    import cross_model_sparse_amd as mf
+    import synth
+    wb = w.with_(H_r=16, H_kv=8)
+    B, e = w.B, synth.DTYPE_BYTES[w.dtype]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    recv_b = [(synth.gen_W(wb, 8100 + i).to(dev), synth.gen_V(wb, 8100 + i).to(dev))
+              for i in range(len(layers))]
+    O_a = torch.empty(w.N, w.H_r, w.d, dtype=synth.torch_dtype(w.dtype), device=dev)
+    O_b = torch.empty(w.N, wb.H_r, w.d, dtype=synth.torch_dtype(w.dtype), device=dev)
+
+    def joint(x, rb):
+        mf.retrieve_fused_multi(x["rp"], x["ci"], x["vals"], x["nnzb"], [(x["W"], x["V"]), rb],
+                                w.N, B, outs=[O_a, O_b])
+
+    def separate(x, rb):
+        mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"], w.N, B, out=O_a)
+        mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], rb[0], rb[1], w.N, B, out=O_b)
+
+    def timed(fn):
+        per_rep = []
+        for rep in range(reps + 1):
+            evs = []
+            for x, rb in zip(layers, recv_b):
+                a, b = ev(), ev()
+                a.record(stream)
+                fn(x, rb)
+                b.record(stream)
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            if rep:
+                per_rep.append(sum(a.elapsed_time(b) for a, b in evs) / len(layers))
+        return float(np.median(per_rep))
+
+    t_joint = timed(joint)
+    t_sep = timed(separate)
+    nz = float(np.mean([x["nnzb"] for x in layers]))
+    T = w.T
+    alg = (nz * w.H_s * B * B * e + w.N * (w.H_kv + wb.H_kv) * w.d * e
+           + w.N * (w.H_r + wb.H_r) * w.d * e + 4 * (T + 1 + nz) + 4 * (w.H_r + wb.H_r) * w.H_s)
+    return {
+        "workload": f"pair14b8b-bf16 sender states ({len(layers)} layers, N={w.N}, B={B}, H_s={w.H_s}) "
+                    f"feeding receivers (H_r={w.H_r}, H_kv={w.H_kv}) and (H_r={wb.H_r}, H_kv={wb.H_kv}), d={w.d}",
+        "ms_per_layer": {"joint_launch": t_joint, "two_launches": t_sep},
+        "query_tokens_per_s_per_layer_both_receivers": {"joint_launch": w.N / t_joint * 1e3,
+                                                        "two_launches": w.N / t_sep * 1e3},
+        "roofline_joint": {"bound": "hbm", "bytes": alg, "achieved": alg / t_joint / 1e6,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": alg / t_joint / 1e6 / HBM_PEAK_GBS},
     }
 
 

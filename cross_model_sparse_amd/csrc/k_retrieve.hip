@@ -153,15 +153,30 @@ __device__ __forceinline__ unsigned short bf16_bits(float f) {
 // Packed batches
 // ---------------------------------------------------------------------------
 
-// A packed batch of sequences.  Kernels take it with kVar = true; with kVar =
-// false they see one sequence of N tokens whose block rows are the whole
-// row_ptr, and the batch fields are not read.
+// One receiver of a sender's BSR state: its head map, values and output.
+struct Recv {
+  const float* W;
+  const void* V;
+  void* O;
+  int64_t ldV, ldO;
+  int H_r, RPW, G;
+};
+constexpr int kMaxRecvSets = 4;
+
+// The general form of a launch: a packed batch of sequences (cu_rows null:
+// one sequence of N tokens whose block rows are the whole row_ptr), tiles
+// optionally read through a block table, and up to kMaxRecvSets receivers fed
+// from the same BSR state.  Kernels take it with kVar = true; with kVar =
+// false they see one sequence and one receiver (the kernel arguments) and the
+// batch fields are not read.
 struct Batch {
   const int32_t* cu_rows;      // [S+1] first global block row of each sequence
   const int32_t* cu_seqlens;   // [S+1] first token of each sequence in V and O
   const int32_t* block_table;  // [nnzb] pool page of each kept block, or nullptr
   int64_t n_pages;             // tiles in the pool (bounds block_table entries)
   int S;
+  int n_recv;                  // receivers; more than 1: recv[] replaces W, V, O
+  Recv recv[kMaxRecvSets];
 };
 
 // The sequence of global block row Ig: its local row I, block rows T, tokens
@@ -172,7 +187,7 @@ struct RowView {
 };
 template <bool kVar>
 __device__ __forceinline__ bool row_view(const Batch& bt, int Ig, int N, int B, RowView& rv) {
-  if (!kVar) {
+  if (!kVar || bt.cu_rows == nullptr) {
     rv.I = Ig;
     rv.N = N;
     rv.T = (N + B - 1) / B;
@@ -271,8 +286,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   __shared__ __align__(16) unsigned char smem[kSmem];
 
   const int subs = B / kRows;
+  int bid = blockIdx.x;
+  if constexpr (kVar) {
+    // several receivers: the work items of one (row, slice) for each receiver
+    // are consecutive among the workgroups one XCD receives (index b, b+8,
+    // b+16, ...), so they run together and read the row's tiles from that
+    // XCD's L2 after the first one has fetched them
+    if (bt.n_recv > 1) {
+      const int local = bid >> 3;
+      const Recv& rc = bt.recv[local % bt.n_recv];
+      bid = (bid & 7) | ((local / bt.n_recv) << 3);
+      W = rc.W;
+      H_r = rc.H_r;
+      RPW = rc.RPW;
+      G = rc.G;
+      V = reinterpret_cast<const unsigned short*>(rc.V);
+      ldV = rc.ldV;
+      O = reinterpret_cast<unsigned short*>(rc.O);
+      ldO = rc.ldO;
+    }
+  }
   int Ig, sub;                                   // global block row, 16-row slice
-  if (!item_of(blockIdx.x, subs, R, RG, &Ig, &sub)) return;
+  if (!item_of(bid, subs, R, RG, &Ig, &sub)) return;
   RowView rv;
   if (!row_view<kVar>(bt, Ig, N, B, rv)) return;
   const int I = rv.I;                            // block row within its sequence
@@ -756,7 +791,9 @@ int launch_simple(int B, int d, const int32_t* row_ptr, const int32_t* col_idx,
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-template <bool kBF16, int NPAIR>
+// kGeneral: always the batch instantiation (several receivers); otherwise the
+// batch instantiation exactly when bt describes a packed batch.
+template <bool kBF16, int NPAIR, bool kGeneral = false>
 int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
                   const int32_t* col_idx, const unsigned short* vals, int64_t nnzb,
                   int H_s, int N, int B, int lg_ncc, const float* W, int H_r, int RPW,
@@ -764,7 +801,7 @@ int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
                   int64_t ldO, int RG, const Batch& bt, int R) {
 #define MF_CASE(NCH_)                                                                            \
   case NCH_:                                                                                     \
-    if (bt.cu_rows)                                                                              \
+    if (kGeneral || bt.cu_rows)                                                                  \
       hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR, true>), grid, dim3(kThreads), 0, st, \
                          row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
                          V, ldV, O, ldO, RG, bt, R);                                             \
@@ -843,9 +880,50 @@ int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     int B, const float* W, int H_r, const void* V, int H_kv,
                     int d, int64_t ldV, void* O, int64_t ldO, void*, size_t,
                     hipStream_t st) {
-  const Batch bt{nullptr, nullptr, nullptr, nnzb, 1};
+  const Batch bt{nullptr, nullptr, nullptr, nnzb, 1, 1, {}};
   return retrieve_impl(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W, H_r, V, H_kv, d, ldV,
                        O, ldO, bt, blocks_of(N, B), st);
+}
+
+int launch_retrieve_multi(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                          int64_t nnzb, int dt, int H_s, int N, int B, int n_recv,
+                          const float* const* W, const int* H_r, const void* const* V,
+                          const int* H_kv, int d, const int64_t* ldV, void* const* O,
+                          const int64_t* ldO, hipStream_t st) {
+  bool together = n_recv > 1 && n_recv <= kMaxRecvSets;
+  for (int i = 0; i < n_recv && together; ++i)
+    together = retrieve_uses_mfma(dt, H_s, B, H_r[i], H_kv[i], d, vals, V[i], ldV[i], O[i], ldO[i]);
+  if (!together) {                               // one launch per receiver, same arithmetic
+    for (int i = 0; i < n_recv; ++i) {
+      const int r = launch_retrieve(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W[i], H_r[i], V[i],
+                                    H_kv[i], d, ldV[i], O[i], ldO[i], nullptr, 0, st);
+      if (r != MF_OK) return r;
+    }
+    return MF_OK;
+  }
+  Batch bt{nullptr, nullptr, nullptr, nnzb, 1, n_recv, {}};
+  int max_rpw = 0;
+  for (int i = 0; i < n_recv; ++i) {
+    bt.recv[i] = Recv{W[i], V[i], O[i], ldV[i], ldO[i], H_r[i], H_r[i] / 8, H_r[i] / H_kv[i]};
+    max_rpw = std::max(max_rpw, H_r[i] / 8);
+  }
+  const int R = blocks_of(N, B);
+  const int RG = std::max(1, R / 16);
+  const int groups = (R + RG - 1) / RG;
+  const int rows_per_xcd = ((groups + 7) / 8) * RG;
+  const dim3 grid(rows_per_xcd * 8 * (B / kRows) * n_recv);
+  const int NCH = (H_s + 7) / 8;
+  const int lg_ncc = B == 16 ? 0 : B == 32 ? 1 : B == 64 ? 2 : 3;
+  auto vp = reinterpret_cast<const unsigned short*>(vals);
+  const Recv& r0 = bt.recv[0];
+  auto V0 = reinterpret_cast<const unsigned short*>(r0.V);
+  auto O0 = reinterpret_cast<unsigned short*>(r0.O);
+  const bool bf = dt == MF_BF16;
+  if (max_rpw > 2)
+    return bf ? launch_mfma_p<true, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
+              : launch_mfma_p<false, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
+  return bf ? launch_mfma_p<true, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
+            : launch_mfma_p<false, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
 }
 
 int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
@@ -854,7 +932,7 @@ int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_
                            int64_t nnzb, int dt, int H_s, int B, const float* W, int H_r,
                            const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
                            hipStream_t st) {
-  const Batch bt{cu_rows, cu_seqlens, block_table, block_table ? n_pages : nnzb, S};
+  const Batch bt{cu_rows, cu_seqlens, block_table, block_table ? n_pages : nnzb, S, 1, {}};
   return retrieve_impl(row_ptr, col_idx, vals, nnzb, dt, H_s, 0, B, W, H_r, V, H_kv, d, ldV,
                        O, ldO, bt, R, st);
 }

@@ -277,6 +277,32 @@ int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                              (hipStream_t)stream);
 }
 
+int mf_retrieve_fused_multi(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                            int64_t nnzb, int dtype, int H_s, int N, int B, int n_recv,
+                            const float* const* W, const int* H_r, const void* const* V,
+                            const int* H_kv, int d, const int64_t* ldV, void* const* O,
+                            const int64_t* ldO, void* stream) {
+  const char* fn = "mf_retrieve_fused_multi";
+  if (n_recv < 1 || n_recv > 4)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": n_recv must be in [1, 4] (got %lld)", n_recv));
+  if (!W || !H_r || !V || !H_kv || !ldV || !O || !ldO)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null receiver array");
+  if (!row_ptr) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": nnzb < 0");
+  if (nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with nnzb > 0");
+  for (int i = 0; i < n_recv; ++i) {
+    const std::string fi = std::string(fn) + fmt(" (receiver %lld)", i);
+    const int st = check_retrieve_shape(fi.c_str(), dtype, H_s, N, B, H_r[i], H_kv[i], d, ldV[i], ldO[i]);
+    if (st != MF_OK) return st;
+    if (!W[i] || !V[i] || !O[i]) return mf::fail(MF_ERR_INVALID, fi + ": null pointer");
+    for (int j = 0; j < i; ++j)
+      if (O[j] == O[i]) return mf::fail(MF_ERR_INVALID, fi + ": output shared with another receiver");
+  }
+  return mf::launch_retrieve_multi(row_ptr, col_idx, vals, nnzb, dtype, H_s, N, B, n_recv, W, H_r, V,
+                                   H_kv, d, ldV, O, ldO, (hipStream_t)stream);
+}
+
 int mf_retrieve_fused_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
                              const int32_t* row_ptr, const int32_t* col_idx,
                              const int32_t* block_table, const void* vals, int64_t n_pages,

@@ -48,6 +48,12 @@ int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     int B, const float* W, int H_r, const void* V, int H_kv,
                     int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
                     size_t workspace_bytes, hipStream_t st);
+// Several receivers (host arrays of n_recv entries) fed from one BSR state.
+int launch_retrieve_multi(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                          int64_t nnzb, int dt, int H_s, int N, int B, int n_recv,
+                          const float* const* W, const int* H_r, const void* const* V,
+                          const int* H_kv, int d, const int64_t* ldV, void* const* O,
+                          const int64_t* ldO, hipStream_t st);
 // One launch over a packed batch of S sequences (R block rows in total).
 int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,
                            const int32_t* row_ptr, const int32_t* col_idx,

@@ -26,7 +26,7 @@ EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mas
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
             "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
-            "mf_retrieve_fused_varlen")
+            "mf_retrieve_fused_multi", "mf_retrieve_fused_varlen")
 
 
 class MapflowError(RuntimeError):
@@ -94,6 +94,10 @@ def load() -> ctypes.CDLL:
     L.mf_retrieve_fused.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
                                     c_vp, c_int, c_vp, c_int, c_int, c_i64, c_vp, c_i64,
                                     c_vp, c_sz, c_vp]
+    L.mf_retrieve_fused_multi.restype = c_int
+    L.mf_retrieve_fused_multi.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
+                                          c_int, c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_vp, c_vp,
+                                          c_vp]
     L.mf_retrieve_fused_varlen.restype = c_int
     L.mf_retrieve_fused_varlen.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_i64, c_i64, c_int, c_int, c_int, c_vp, c_int,
@@ -247,6 +251,38 @@ def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Ten
                                     V.stride(0), _ptr(out), out.stride(0), _ptr(workspace),
                                     ws_bytes, _stream(stream)))
     return out
+
+
+def retrieve_fused_multi(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                         nnzb: int, receivers, N: int, B: int, outs=None, stream=None) -> list:
+    """One sender BSR state feeding several receivers (mf_retrieve_fused_multi).
+    receivers: a sequence of (W [H_r][H_s] fp32, V [N][H_kv][d]) pairs; returns
+    the list of outputs O_i [N][H_r_i][d] (or fills `outs`)."""
+    n = len(receivers)
+    _need_cuda(row_ptr, col_idx, vals, *[t for rv in receivers for t in rv])
+    H_s = vals.shape[1]
+    if outs is None:
+        outs = [torch.empty(N, W.shape[0], V.shape[2], dtype=V.dtype, device=V.device)
+                for W, V in receivers]
+    for (W, V), O in zip(receivers, outs):
+        if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != H_s:
+            raise MapflowError(MF_ERR_INVALID, "W must be a contiguous fp32 [H_r][H_s] tensor")
+        if V.dim() != 3 or V.stride(2) != 1 or V.stride(1) != V.shape[2] or V.dtype != vals.dtype:
+            raise MapflowError(MF_ERR_INVALID, "V must be [N][H_kv][d] with contiguous rows, dtype of vals")
+        if O.dim() != 3 or O.stride(2) != 1 or O.stride(1) != O.shape[2]:
+            raise MapflowError(MF_ERR_INVALID, "out must be [N][H_r][d] with contiguous rows")
+    d = receivers[0][1].shape[2]
+    arr = lambda ctype, xs: (ctype * n)(*xs)
+    _check(load().mf_retrieve_fused_multi(
+        _ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(nnzb), _dcode(vals), H_s, N, B, n,
+        arr(ctypes.c_void_p, [W.data_ptr() for W, _ in receivers]),
+        arr(ctypes.c_int, [W.shape[0] for W, _ in receivers]),
+        arr(ctypes.c_void_p, [V.data_ptr() for _, V in receivers]),
+        arr(ctypes.c_int, [V.shape[1] for _, V in receivers]), d,
+        arr(ctypes.c_int64, [V.stride(0) for _, V in receivers]),
+        arr(ctypes.c_void_p, [O.data_ptr() for O in outs]),
+        arr(ctypes.c_int64, [O.stride(0) for O in outs]), _stream(stream)))
+    return outs
 
 
 def retrieve_fused_varlen(cu_seqlens: torch.Tensor, cu_rows: torch.Tensor,

@@ -244,6 +244,32 @@ int mf_retrieve_fused(const int32_t* row_ptr, const int32_t* col_idx,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One sender state, several receivers (the pages serve several downstream
+ * models from one sender's cached maps: article, second section, and its
+ * three-model experiment).  Computes, for each receiver i, exactly what
+ * mf_retrieve_fused(row_ptr, col_idx, vals, nnzb, dtype, H_s, N, B, W[i],
+ * H_r[i], V[i], H_kv[i], d, ldV[i], O[i], ldO[i]) computes (outputs are bitwise
+ * identical), in one launch when every receiver takes the matrix-core kernel:
+ * the work items of the receivers for one (block row, 16-row slice) run
+ * together on one XCD, so the row's tiles leave HBM once for all receivers.
+ * Otherwise it runs one launch per receiver.
+ *
+ *  n_recv       host, number of receivers, 1..4.
+ *  W, V, O      host arrays of n_recv device pointers (layouts as in
+ *               mf_retrieve_fused); the O buffers must not overlap.
+ *  H_r, H_kv, ldV, ldO   host arrays of n_recv entries.
+ *  The BSR state, dtype, H_s, N, B and d are shared by all receivers.
+ *  Errors: MF_ERR_INVALID for n_recv outside [1, 4], a null array or
+ *  pointer, two receivers with the same O, and every check of
+ *  mf_retrieve_fused on any receiver (the message names the receiver).
+ */
+int mf_retrieve_fused_multi(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
+                            int64_t nnzb, int dtype, int H_s, int N, int B, int n_recv,
+                            const float* const* W, const int* H_r, const void* const* V,
+                            const int* H_kv, int d, const int64_t* ldV, void* const* O,
+                            const int64_t* ldO, void* stream);
+
+/*
  * Fused retrieval over a packed batch of sequences in one launch (the pages'
  * serving integration runs under chunked prefill and paged KV caches: paper
  * page, "Practical Implementation Details").  For each sequence s it computes

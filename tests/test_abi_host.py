@@ -293,3 +293,34 @@ def test_retrieve_varlen_rejects(L, kw, frag):
 def test_retrieve_varlen_empty_batch_launches_nothing(L):
     # R = 0 block rows: valid, nothing to do (no GPU work is queued)
     assert _varlen(L, R=0, nnzb=0, col_idx=None, vals=None) == mf.MF_OK
+
+
+# ---- several receivers ----------------------------------------------------------
+
+def _multi(L, n=2, **kw):
+    import ctypes
+    a = dict(row_ptr=FAKE, col_idx=FAKE, vals=FAKE, nnzb=5, dt=2, H_s=40, N=8192, B=64,
+             W=[FAKE, FAKE + 4096], H_r=[32, 16], V=[FAKE, FAKE + 8192], H_kv=[8, 8], d=128,
+             ldV=[1024, 1024], O=[FAKE, FAKE + 16384], ldO=[4096, 2048])
+    a.update(kw)
+    arr = lambda t, xs: None if xs is None else (t * len(xs))(*xs)
+    return L.mf_retrieve_fused_multi(a["row_ptr"], a["col_idx"], a["vals"], a["nnzb"], a["dt"],
+                                     a["H_s"], a["N"], a["B"], n,
+                                     arr(ctypes.c_void_p, a["W"]), arr(ctypes.c_int, a["H_r"]),
+                                     arr(ctypes.c_void_p, a["V"]), arr(ctypes.c_int, a["H_kv"]),
+                                     a["d"], arr(ctypes.c_int64, a["ldV"]),
+                                     arr(ctypes.c_void_p, a["O"]), arr(ctypes.c_int64, a["ldO"]),
+                                     None)
+
+
+@pytest.mark.parametrize("n,kw,frag", [
+    (0, {}, "n_recv"), (5, {}, "n_recv"), (2, dict(W=None), "null receiver array"),
+    (2, dict(ldO=None), "null receiver array"), (2, dict(row_ptr=None), "null pointer"),
+    (2, dict(nnzb=-1), "nnzb"), (2, dict(vals=None), "null col_idx/vals"),
+    (2, dict(H_r=[32, 30]), "receiver 1"), (2, dict(H_kv=[8, 0]), "multiple of H_kv"),
+    (2, dict(ldV=[1024, 100]), "ldV"), (2, dict(O=[FAKE, FAKE]), "shared"),
+    (2, dict(V=[FAKE, None]), "null pointer"), (2, dict(d=96), "d must"), (2, dict(B=24), "B must"),
+])
+def test_retrieve_multi_rejects(L, n, kw, frag):
+    assert _multi(L, n, **kw) == mf.MF_ERR_INVALID
+    assert frag in _last(L)
