@@ -15,7 +15,7 @@ retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
 bounded sample of block rows of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
-                    [--no-qk] [--no-varlen] [--no-fanout] [--copy-ref-mib M]
+                    [--no-qk] [--no-varlen] [--no-fanout] [--no-cache] [--copy-ref-mib M]
 """
 from __future__ import annotations
 
@@ -47,6 +47,8 @@ def parse():
                     help="skip the packed-batch (varlen) retrieval leg")
     ap.add_argument("--no-fanout", action="store_true",
                     help="skip the one-sender-several-receivers leg")
+    ap.add_argument("--no-cache", action="store_true",
+                    help="skip the Block Manager (prefix cache) leg")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference "
                          "kernel for scaling hardware byte counters)")
@@ -241,6 +243,8 @@ def main():
         out["compress_without_dense_map"] = qk_leg(dev, args.steps)
     if not args.no_fanout:
         out["fanout"] = fanout_leg(dev, w, layers, max(5, args.steps))
+    if not args.no_cache:
+        out["prefix_cache"] = cache_leg(dev, w, layers, max(5, args.steps))
     if not args.no_varlen:
         out["varlen_batch"] = varlen_leg(dev, max(5, args.steps))
     if not args.no_cpu:
@@ -374,6 +378,84 @@ def fanout_leg(dev, w, layers, reps):
         "roofline_joint": {"bound": "hbm", "bytes": alg, "achieved": alg / t_joint / 1e6,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": alg / t_joint / 1e6 / HBM_PEAK_GBS},
+    }
+
+
+def cache_leg(dev, w, layers, reps):
+    """The Block Manager on the step's BSR states: every full block row of all
+    layers (N = 8192 tokens, 128 rows per layer, seeded token ids) is inserted
+    into one manager over a tile pool sized for them, the tiles are copied into
+    their pages (mf_pool_store, HIP events), and the whole prefix is then looked
+    up and released for every layer (host wall time per call).  Layer 0 is then
+    retrieved from the pool through the block table and from its own BSR
+    state (HIP events, medians over `reps`)."""
+    import torch
+    import cross_model_sparse_amd as mf
+    B, N, T = w.B, w.N, w.T
+    e = 2
+    tokens = np.random.default_rng(17).integers(0, 151_000, size=N).astype(np.int32)
+    total = int(sum(x["nnzb"] for x in layers))
+    pool = torch.empty(total, w.H_s, B, B, dtype=layers[0]["vals"].dtype, device=dev)
+    bm = mf.BlockManager(B, len(layers), total, seed=1)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    host = [(x["rp"].cpu().numpy(), x["ci"][: x["nnzb"]].cpu().numpy()) for x in layers]
+    t_ins, t_store, pages_l0 = 0.0, 0.0, None
+    for l, (x, (rp, ci)) in enumerate(zip(layers, host)):
+        t0 = time.perf_counter()
+        pages = bm.insert(l, tokens, 0, rp, ci)
+        t_ins += time.perf_counter() - t0
+        pg = torch.from_numpy(pages).to(dev)
+        a, b = ev(), ev()
+        a.record(stream)
+        mf.pool_store(x["vals"][: x["nnzb"]], pg, pool)
+        b.record(stream)
+        b.synchronize()
+        t_store += a.elapsed_time(b) / 1e3
+        if l == 0:
+            pages_l0 = pg
+    t_look = 0.0
+    for l in range(len(layers)):
+        t0 = time.perf_counter()
+        rp_c, ci_c, pg_c = bm.lookup(l, tokens)
+        bm.release(l, tokens, len(rp_c) - 1)
+        t_look += time.perf_counter() - t0
+        assert len(rp_c) - 1 == T
+    rows = T * len(layers)
+    x = layers[0]
+    cu = torch.tensor([0, N], dtype=torch.int32, device=dev)
+    cr = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    O = torch.empty_like(x["O"])
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_pool = timed(lambda: mf.retrieve_fused_varlen(cu, cr, x["rp"], x["ci"], pool, x["nnzb"], x["W"],
+                                                    x["V"], B, block_table=pages_l0, out=O))
+    t_own = timed(lambda: mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
+                                            N, B, out=O))
+    st = bm.stats()
+    bm.close()
+    store_bytes = 2 * total * w.H_s * B * B * e
+    return {
+        "workload": f"pair14b8b-bf16: {len(layers)} layers x {T} block rows of {B} tokens, "
+                    f"{total} kept blocks in one pool ({total * w.H_s * B * B * e / 1e9:.2f} GB)",
+        "host_us_per_row": {"insert": t_ins / rows * 1e6, "lookup_and_release": t_look / rows * 1e6},
+        "pool_store": {"ms_per_layer": t_store / len(layers) * 1e3,
+                       "achieved_GBs": store_bytes / t_store / 1e9,
+                       "frac_of_hbm_peak": store_bytes / t_store / 1e9 / HBM_PEAK_GBS},
+        "retrieve_layer0_ms": {"from_pool_via_block_table": t_pool, "from_own_bsr": t_own},
+        "manager_stats": st,
     }
 
 

@@ -178,6 +178,10 @@ struct Batch {
   int n_recv;                  // receivers; more than 1: recv[] replaces W, V, O
   Recv recv[kMaxRecvSets];
 };
+// The kernels take the batch's index arrays (cu_rows, cu_seqlens,
+// block_table) again as separate read-only, non-aliased arguments: read
+// through the struct they become vector loads, each followed by a wait on
+// every outstanding tile copy; as restrict arguments they are scalar loads.
 
 // The sequence of global block row Ig: its local row I, block rows T, tokens
 // N and first token tok0.  False when the row holds no query row.
@@ -186,8 +190,10 @@ struct RowView {
   int64_t tok0;
 };
 template <bool kVar>
-__device__ __forceinline__ bool row_view(const Batch& bt, int Ig, int N, int B, RowView& rv) {
-  if (!kVar || bt.cu_rows == nullptr) {
+__device__ __forceinline__ bool row_view(const Batch& bt, const int32_t* __restrict__ cu_rows,
+                                         const int32_t* __restrict__ cu_seqlens, int Ig, int N,
+                                         int B, RowView& rv) {
+  if (!kVar || cu_rows == nullptr) {
     rv.I = Ig;
     rv.N = N;
     rv.T = (N + B - 1) / B;
@@ -197,20 +203,34 @@ __device__ __forceinline__ bool row_view(const Batch& bt, int Ig, int N, int B, 
   int lo = 0, hi = bt.S - 1;                     // last s with cu_rows[s] <= Ig
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (bt.cu_rows[mid] <= Ig) lo = mid; else hi = mid - 1;
+    if (cu_rows[mid] <= Ig) lo = mid; else hi = mid - 1;
   }
-  rv.I = Ig - bt.cu_rows[lo];
-  rv.T = bt.cu_rows[lo + 1] - bt.cu_rows[lo];
-  rv.tok0 = bt.cu_seqlens[lo];
-  rv.N = bt.cu_seqlens[lo + 1] - bt.cu_seqlens[lo];
+  rv.I = Ig - cu_rows[lo];
+  rv.T = cu_rows[lo + 1] - cu_rows[lo];
+  rv.tok0 = cu_seqlens[lo];
+  rv.N = cu_seqlens[lo + 1] - cu_seqlens[lo];
   return rv.I >= 0 && rv.I < rv.T && (int64_t)rv.I * B < rv.N;
 }
+// Table entry of kept block k (k itself without a table), unchecked: the
+// retrieval loop loads it a phase before it checks it with page_ok, so that
+// the load's latency stays off the copy issue.  The load is issued either way
+// (from col_idx, a valid address for every k < nnzb, when there is no table):
+// a load inside a branch gets a wait of its own at the branch's end.
+template <bool kVar>
+__device__ __forceinline__ int64_t page_raw(const int32_t* __restrict__ block_table,
+                                            const int32_t* __restrict__ col_idx, int64_t k) {
+  if (!kVar) return k;
+  const int64_t v = (block_table ? block_table : col_idx)[k];
+  return block_table ? v : k;
+}
+__device__ __forceinline__ bool page_ok(const Batch& bt, int64_t p) { return p >= 0 && p < bt.n_pages; }
 // Pool page of kept block k, or -1 when the table points outside the pool.
 template <bool kVar>
-__device__ __forceinline__ int64_t page_of(const Batch& bt, int64_t k) {
-  if (!kVar || bt.block_table == nullptr) return k;
-  const int64_t p = bt.block_table[k];
-  return (p >= 0 && p < bt.n_pages) ? p : -1;
+__device__ __forceinline__ int64_t page_of(const Batch& bt, const int32_t* __restrict__ block_table,
+                                           int64_t k) {
+  if (!kVar || block_table == nullptr) return k;
+  const int64_t p = block_table[k];
+  return page_ok(bt, p) ? p : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -268,7 +288,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N, int B,
     int lg_ncc, const float* __restrict__ W, int H_r, int RPW, int G,
     const unsigned short* __restrict__ V, int64_t ldV,
-    unsigned short* __restrict__ O, int64_t ldO, int RG, Batch bt, int R) {
+    unsigned short* __restrict__ O, int64_t ldO, int RG, Batch bt,
+    const int32_t* __restrict__ cu_rows, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ block_table, int R) {
   using Plan = HmPlan<kBF16, NCH>;
   constexpr int NBOP = Plan::NBOP;
   constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   int Ig, sub;                                   // global block row, 16-row slice
   if (!item_of(bid, subs, R, RG, &Ig, &sub)) return;
   RowView rv;
-  if (!row_view<kVar>(bt, Ig, N, B, rv)) return;
+  if (!row_view<kVar>(bt, cu_rows, cu_seqlens, Ig, N, B, rv)) return;
   const int I = rv.I;                            // block row within its sequence
   const int T = rv.T;
   N = rv.N;
@@ -386,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   auto col_of = [&](int x) -> int {
     const int64_t k = block_of(x);
     if constexpr (!kVar) return col_idx[k];
-    else return page_of<kVar>(bt, k) >= 0 ? col_idx[k] : -1;
+    else return page_of<kVar>(bt, block_table, k) >= 0 ? col_idx[k] : -1;
   };
 
   // tile-slice copy d of this wavefront: 1 KB piece pr = wave + 8d (heads 2pr,
@@ -404,17 +426,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   const unsigned smem_lds = lds_addr(smem);
   // chunk x covers keys 16 * ((x + sub) mod B/16) of its block: the row
   // slices of one block row take the block's chunks in staggered order
-  auto vals_src = [&](int x) -> const unsigned short* {
+  // (with a block table the page of chunk x is passed in: the loop loads it
+  // one phase ahead, so its latency stays out of the copy issue)
+  auto vals_src = [&](int x, int64_t pg = 0) -> const unsigned short* {
     const int xc = x < n_chunks ? x : n_chunks - 1;
     if constexpr (!kVar) return vals + block_of(x) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
-    const int64_t pg = page_of<kVar>(bt, block_of(x));
-    return vals + (pg < 0 ? 0 : pg) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
+    return vals + (page_ok(bt, pg) ? pg : 0) * H_s * tile + ((xc + sub) & ncc_mask) * kCB;
   };
   auto copy_piece = [&](const unsigned short* src, int slot, int d) {
     if (d < ndv_w) dma16s(head_off[d], src, smem_lds + slot * kStage + (wave + kWaves * d) * 1024);
   };
   auto issue_vals = [&](int x, int slot) {
-    const unsigned short* src = vals_src(x);
+    const unsigned short* src = vals_src(x, page_of<kVar>(bt, block_table, block_of(x)));
 #pragma unroll
     for (int d = 0; d < NDV; ++d) copy_piece(src, slot, d);
   };
@@ -628,11 +651,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     wait_vm_n((NSTG - 2) * ndv_w);               // slice 1 landed
     lds_barrier();
   }
+  int64_t pg_n = 0;                              // table entry of chunk u + NSTG
+  if constexpr (kVar) pg_n = page_raw<kVar>(block_table, col_idx, block_of(NSTG));
   for (int u = 0; u < n_chunks; ++u) {
-    const int Jn = col_of(u + 2);
+    // column (and, with a table, page) of chunk u+2: loaded now, combined
+    // after this phase's barrier, so neither load waits inside the phase
+    const int64_t kn = block_of(u + 2);
+    const int Jn_col = col_idx[kn];
+    int64_t pg_J = 0;
+    if constexpr (kVar) pg_J = page_raw<kVar>(block_table, col_idx, kn);
     u32x4 vt[4];
     read_vt(vt);
-    const unsigned short* vsrc = vals_src(u + NSTG);
+    const unsigned short* vsrc = vals_src(u + NSTG, pg_n);
+    if constexpr (kVar) pg_n = page_raw<kVar>(block_table, col_idx, block_of(u + NSTG + 1));
     const int cur = slot;
     const int s1 = slot + 1 == NSTG ? 0 : slot + 1;
     auto mid_copy = [&]() {
@@ -649,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vt, mid_copy, step_copy);
     wait_vm_n((NSTG - 2) * ndv_w);               // V(u+1) and slice u+2 landed
     lds_barrier();
-    J1 = Jn;
+    J1 = (!kVar || page_ok(bt, pg_J)) ? Jn_col : -1;
     slot = s1;
   }
   wait_vm<0>();
@@ -694,14 +725,16 @@ __global__ __launch_bounds__(kSimpleThreads) void k_retrieve_simple(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const typename TT::S* __restrict__ vals, int64_t nnzb, int H_s, int N,
     const float* __restrict__ W, int H_r, const typename TT::S* __restrict__ V,
-    int H_kv, int64_t ldV, typename TT::S* __restrict__ O, int64_t ldO, Batch bt, int R) {
+    int H_kv, int64_t ldV, typename TT::S* __restrict__ O, int64_t ldO, Batch bt,
+    const int32_t* __restrict__ cu_rows, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ block_table, int R) {
   constexpr int RPP = kSimpleThreads / D;        // query rows per pass
   constexpr int NACC = BB / RPP;           // rows per thread
   __shared__ float ahat[BB * BB];
   __shared__ float wrow[64];
   const int Ig = R - 1 - (int)blockIdx.x;        // global block row, last first
   RowView rv;
-  if (!row_view<kVar>(bt, Ig, N, BB, rv)) return;
+  if (!row_view<kVar>(bt, cu_rows, cu_seqlens, Ig, N, BB, rv)) return;
   const int T = rv.T;
   const int I = rv.I;
   N = rv.N;
@@ -722,7 +755,7 @@ __global__ __launch_bounds__(kSimpleThreads) void k_retrieve_simple(
   __syncthreads();
   for (int64_t k = kb; k < ke; ++k) {
     const int J = col_idx[k];
-    const int64_t pg = page_of<kVar>(bt, k);
+    const int64_t pg = page_of<kVar>(bt, block_table, k);
     if (J < 0 || J >= T || pg < 0) continue;
     const typename TT::S* blk = vals + pg * H_s * BB * BB;
     for (int e = tid; e < BB * BB; e += kSimpleThreads) {
@@ -757,12 +790,14 @@ int launch_simple_t(const int32_t* row_ptr, const int32_t* col_idx, const void* 
     hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D, true>), dim3(R, H_r), dim3(kSimpleThreads),
                        0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
                        nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
-                       ldV, reinterpret_cast<S*>(O), ldO, bt, R);
+                       ldV, reinterpret_cast<S*>(O), ldO, bt, bt.cu_rows, bt.cu_seqlens,
+                       bt.block_table, R);
   else
     hipLaunchKernelGGL((k_retrieve_simple<TT, BB, D, false>), dim3(R, H_r), dim3(kSimpleThreads),
                        0, st, row_ptr, col_idx, reinterpret_cast<const S*>(vals),
                        nnzb, H_s, N, W, H_r, reinterpret_cast<const S*>(V), H_kv,
-                       ldV, reinterpret_cast<S*>(O), ldO, bt, R);
+                       ldV, reinterpret_cast<S*>(O), ldO, bt, bt.cu_rows, bt.cu_seqlens,
+                       bt.block_table, R);
   return mf::hip_check(hipGetLastError(), "k_retrieve_simple launch");
 }
 
@@ -804,11 +839,11 @@ int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
     if (kGeneral || bt.cu_rows)                                                                  \
       hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR, true>), grid, dim3(kThreads), 0, st, \
                          row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
-                         V, ldV, O, ldO, RG, bt, R);                                             \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
     else                                                                                         \
       hipLaunchKernelGGL((k_retrieve_mfma<kBF16, NCH_, NPAIR, false>), grid, dim3(kThreads), 0, st, \
                          row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
-                         V, ldV, O, ldO, RG, bt, R);                                             \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
     break;
   switch (NCH) {
     MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5) MF_CASE(6)

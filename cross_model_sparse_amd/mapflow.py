@@ -26,7 +26,9 @@ EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mas
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
             "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
-            "mf_retrieve_fused_multi", "mf_retrieve_fused_varlen")
+            "mf_retrieve_fused_multi", "mf_retrieve_fused_varlen", "mf_prefix_hashes",
+            "mf_bm_create", "mf_bm_destroy", "mf_bm_lookup", "mf_bm_release", "mf_bm_insert",
+            "mf_bm_stats", "mf_pool_store")
 
 
 class MapflowError(RuntimeError):
@@ -98,6 +100,23 @@ def load() -> ctypes.CDLL:
     L.mf_retrieve_fused_multi.argtypes = [c_vp, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int,
                                           c_int, c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_vp, c_vp,
                                           c_vp]
+    c_u64 = ctypes.c_uint64
+    L.mf_prefix_hashes.restype = c_int
+    L.mf_prefix_hashes.argtypes = [c_vp, c_i64, c_int, c_u64, c_vp]
+    L.mf_bm_create.restype = c_vp
+    L.mf_bm_create.argtypes = [c_int, c_int, c_i64, c_u64]
+    L.mf_bm_destroy.restype = None
+    L.mf_bm_destroy.argtypes = [c_vp]
+    L.mf_bm_lookup.restype = c_int
+    L.mf_bm_lookup.argtypes = [c_vp, c_int, c_vp, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_i64]
+    L.mf_bm_release.restype = c_int
+    L.mf_bm_release.argtypes = [c_vp, c_int, c_vp, c_i64, c_int]
+    L.mf_bm_insert.restype = c_int
+    L.mf_bm_insert.argtypes = [c_vp, c_int, c_vp, c_i64, c_int, c_int, c_vp, c_vp, c_vp]
+    L.mf_bm_stats.restype = c_int
+    L.mf_bm_stats.argtypes = [c_vp, c_vp]
+    L.mf_pool_store.restype = c_int
+    L.mf_pool_store.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp]
     L.mf_retrieve_fused_varlen.restype = c_int
     L.mf_retrieve_fused_varlen.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_i64, c_i64, c_int, c_int, c_int, c_vp, c_int,
@@ -425,3 +444,92 @@ def compress(A: torch.Tensor, B: int, p: float, cap_nnzb: int | None = None, str
     row_ptr, col_idx, vals, nnzb = topp_select_bsr(mass, A, B, p, cap_nnzb=cap_nnzb,
                                                    stream=stream)
     return mass, row_ptr, col_idx, vals, nnzb
+
+
+# ---- Block Manager -----------------------------------------------------------
+
+def _i32_host(a) -> "np.ndarray":
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def prefix_hashes(tokens, B: int, seed: int = 0):
+    """uint64 prefix hashes h_1..h_n of the full B-token chunks (mf_prefix_hashes)."""
+    import numpy as np
+    tok = _i32_host(tokens)
+    out = np.zeros(len(tok) // B, dtype=np.uint64)
+    _check(load().mf_prefix_hashes(tok.ctypes.data, len(tok), B, seed, out.ctypes.data))
+    return out
+
+
+class BlockManager:
+    """Prefix-hash index of cached BSR block rows (mf_bm_*); host bookkeeping
+    for a caller-owned device tile pool of n_pages pages."""
+
+    STATS = ("free_pages", "cached_rows", "held_rows", "hits", "misses", "evictions", "inserted")
+
+    def __init__(self, B: int, n_layers: int, n_pages: int, seed: int = 0):
+        self._L = load()
+        self._m = self._L.mf_bm_create(B, n_layers, n_pages, seed)
+        if not self._m:
+            raise MapflowError(MF_ERR_INVALID, self._L.mf_last_error().decode())
+        self.B, self.n_layers, self.n_pages = B, n_layers, n_pages
+
+    def close(self):
+        if getattr(self, "_m", None):
+            self._L.mf_bm_destroy(self._m)
+            self._m = None
+
+    def __del__(self):
+        self.close()
+
+    def lookup(self, layer: int, tokens, max_rows: int | None = None, cap: int | None = None):
+        """(row_ptr, col_idx, pages) numpy int32 of the longest cached prefix; the
+        returned rows stay held until release()."""
+        import numpy as np
+        tok = _i32_host(tokens)
+        n = len(tok) // self.B if max_rows is None else int(max_rows)
+        if cap is None:
+            cap = self.n_pages
+        row_ptr = np.zeros(n + 1, dtype=np.int32)
+        col = np.zeros(max(cap, 1), dtype=np.int32)
+        pages = np.zeros(max(cap, 1), dtype=np.int32)
+        nr = ctypes.c_int(0)
+        _check(self._L.mf_bm_lookup(self._m, layer, tok.ctypes.data, len(tok), n, ctypes.byref(nr),
+                                    row_ptr.ctypes.data, col.ctypes.data, pages.ctypes.data, cap))
+        k = int(row_ptr[nr.value])
+        return row_ptr[: nr.value + 1].copy(), col[:k].copy(), pages[:k].copy()
+
+    def release(self, layer: int, tokens, n_rows: int):
+        tok = _i32_host(tokens)
+        _check(self._L.mf_bm_release(self._m, layer, tok.ctypes.data, len(tok), int(n_rows)))
+
+    def insert(self, layer: int, tokens, row0: int, row_ptr, col_idx):
+        """Caches rows row0.. (row_ptr from 0); returns the pages (numpy int32,
+        -1 for rows already cached) to copy the tiles into."""
+        import numpy as np
+        tok, rp, ci = _i32_host(tokens), _i32_host(row_ptr), _i32_host(col_idx)
+        pages = np.full(max(int(rp[-1]), 1), -1, dtype=np.int32)
+        _check(self._L.mf_bm_insert(self._m, layer, tok.ctypes.data, len(tok), int(row0),
+                                    len(rp) - 1, rp.ctypes.data, ci.ctypes.data if len(ci) else None,
+                                    pages.ctypes.data))
+        return pages[: int(rp[-1])]
+
+    def stats(self) -> dict:
+        import numpy as np
+        out = np.zeros(7, dtype=np.int64)
+        _check(self._L.mf_bm_stats(self._m, out.ctypes.data))
+        return dict(zip(self.STATS, (int(x) for x in out)))
+
+
+def pool_store(vals: torch.Tensor, pages: torch.Tensor, pool: torch.Tensor, stream=None):
+    """pool[pages[k]] = vals[k] on the device (mf_pool_store); pages outside
+    the pool (e.g. -1) are skipped."""
+    _need_cuda(vals, pages, pool)
+    if pages.dtype != torch.int32 or not pages.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "pages must be a contiguous int32 tensor")
+    if vals.dtype != pool.dtype or vals.shape[1:] != pool.shape[1:]:
+        raise MapflowError(MF_ERR_INVALID, "vals and pool must share dtype and tile shape")
+    n = min(vals.shape[0], pages.numel())
+    _check(load().mf_pool_store(_ptr(vals), n, _ptr(pages), _ptr(pool), pool.shape[0],
+                                _dcode(vals), vals.shape[1], vals.shape[2], _stream(stream)))

@@ -31,7 +31,8 @@
  *    mf_topp_select_bsr.
  *  - Dtype codes: MF_F32 = 0, MF_F16 = 1, MF_BF16 = 2.
  *  - The library holds no global state besides the thread-local error text
- *    and is safe to call from several host threads on different streams.
+ *    (a Block Manager is an object the caller creates and destroys) and is
+ *    safe to call from several host threads on different streams.
  */
 #ifndef MAPFLOW_H
 #define MAPFLOW_H
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 3
+#define MF_ABI_VERSION 4
 
 typedef enum {
   MF_OK = 0,
@@ -311,6 +312,90 @@ int mf_retrieve_fused_varlen(int S, int R, const int32_t* cu_seqlens, const int3
                              int64_t nnzb, int dtype, int H_s, int B, const float* W, int H_r,
                              const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block Manager: the prefix-hash index of cached compressed state (paper
+ * page, "Practical Implementation Details": the cache is organised by a Block
+ * Manager with a prefix-hash index; article, third section, second component:
+ * each index key carries the information of the whole preceding context).
+ *
+ * Block row I of a sender layer's causal map depends on tokens 0..(I+1)B-1
+ * only, so it is cached under the chained hash of exactly that prefix:
+ *   h_0 = seed,
+ *   h_{c+1} = FNV-1a 64-bit over (h_c as 8 little-endian bytes, then tokens
+ *             cB .. cB+B-1 as 4 little-endian bytes each)
+ * (FNV-1a: offset basis 14695981039346656037, prime 1099511628211), and block
+ * row I of layer l is keyed by (l, h_{I+1}).  Only full chunks of B tokens are
+ * cached.  An entry holds the row's kept column blocks and, per kept block,
+ * the page of a caller-owned device tile pool [n_pages][H_s][B][B] that holds
+ * its tiles.  It also keeps the parent hash and the chunk's tokens: lookups
+ * compare both, so a hash collision can only make a row look absent.
+ *
+ * Pages are handed out smallest index first.  When too few are free, rows
+ * that no lookup holds are evicted, least recently used first (a lookup or an
+ * insert that meets a row counts as a use).  The manager is host memory only,
+ * created and destroyed by the caller; each call takes the manager's mutex,
+ * so one manager may be shared by host threads.  Tiles move with
+ * mf_pool_store.
+ * ---------------------------------------------------------------------- */
+typedef struct mf_block_manager mf_block_manager;
+
+/* The prefix hashes h_1 .. h_n of the n = n_tokens / B full chunks.
+ *  tokens  host, [n_tokens] int32;  hashes  host, [n] uint64, written.
+ *  Errors: MF_ERR_INVALID for B < 1, n_tokens < 0, null pointers. */
+int mf_prefix_hashes(const int32_t* tokens, int64_t n_tokens, int B, uint64_t seed,
+                     uint64_t* hashes);
+
+/* A manager for block size B, n_layers sender layers and a pool of n_pages
+ * tile pages, hashing from `seed` (e.g. one per sender model).  Returns NULL
+ * (with mf_last_error set) for B < 1, n_layers < 1 or n_pages outside
+ * [0, 2^31-1]. */
+mf_block_manager* mf_bm_create(int B, int n_layers, int64_t n_pages, uint64_t seed);
+
+/* Frees the manager (not the pool).  NULL is accepted. */
+void mf_bm_destroy(mf_block_manager* m);
+
+/* The longest cached prefix of `tokens` for `layer`, at most max_rows block
+ * rows: *n_rows rows, row_ptr[0..*n_rows] (host, from 0), col_idx and pages
+ * (host, row_ptr[*n_rows] entries; cap is their capacity).  Every returned
+ * row is held (never evicted) until mf_bm_release.
+ * Errors: MF_ERR_INVALID for a null manager / n_rows / row_ptr, a layer
+ * outside [0, n_layers), negative sizes, cap > 0 with null col_idx / pages;
+ * MF_ERR_CAPACITY when the rows hold more than cap blocks (*n_rows is then
+ * set and nothing is held). */
+int mf_bm_lookup(mf_block_manager* m, int layer, const int32_t* tokens, int64_t n_tokens,
+                 int max_rows, int* n_rows, int32_t* row_ptr, int32_t* col_idx, int32_t* pages,
+                 int64_t cap);
+
+/* Releases the first n_rows rows of `tokens` held by a lookup.
+ * Errors: MF_ERR_INVALID when a row is not held (nothing is released then). */
+int mf_bm_release(mf_block_manager* m, int layer, const int32_t* tokens, int64_t n_tokens,
+                  int n_rows);
+
+/* Caches block rows row0 .. row0+n_rows-1 of `tokens` for `layer`: the
+ * rows' kept columns as row_ptr[n_rows+1] (host, from 0) and col_idx (host,
+ * ascending per row, each <= its row).  pages_out (host, row_ptr[n_rows]
+ * entries) receives the pool page assigned to each kept block, or -1 for the
+ * blocks of rows already cached; the caller then copies the tiles into those
+ * pages (mf_pool_store).  Needs (row0 + n_rows) * B tokens.
+ * Errors: MF_ERR_INVALID for bad arguments; MF_ERR_CAPACITY when not enough
+ * pages are free or evictable (nothing is inserted or evicted then). */
+int mf_bm_insert(mf_block_manager* m, int layer, const int32_t* tokens, int64_t n_tokens,
+                 int row0, int n_rows, const int32_t* row_ptr, const int32_t* col_idx,
+                 int32_t* pages_out);
+
+/* out (host, 7 entries): free pages, cached rows, held rows, row hits, row
+ * misses (chunks a lookup asked for and did not get), evictions, inserted rows. */
+int mf_bm_stats(mf_block_manager* m, int64_t* out);
+
+/* Device copy of kept tiles into pool pages: pool[pages[k]] = vals[k] for
+ * k < nnzb, skipping pages outside [0, n_pages) (e.g. the -1 of rows already
+ * cached).  vals [nnzb][H_s][B][B] and pool [n_pages][H_s][B][B] of `dtype`,
+ * both 16-byte aligned; pages device int32 [nnzb].
+ * Errors: MF_ERR_INVALID for bad dtype / B / H_s, negative sizes, null
+ * pointers or misaligned buffers; MF_ERR_HIP for a failed launch. */
+int mf_pool_store(const void* vals, int64_t nnzb, const int32_t* pages, void* pool,
+                  int64_t n_pages, int dtype, int H_s, int B, void* stream);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mf.abi_version() == 3
+    assert mf.abi_version() == 4
     for st in range(5):
         assert L.mf_status_string(st)
     assert b"unknown" in L.mf_status_string(99)
@@ -201,7 +201,7 @@ def test_binding_refuses_host_tensors():
 def test_header_documents_every_entry_point():
     src = open(HEADER).read()
     for name in declared_functions():
-        m = re.search(r"\n(?:int|size_t|const char\*)\s+" + name + r"\(", src)
+        m = re.search(r"\n(?:int|size_t|void|const char\*|mf_block_manager\*)\s+" + name + r"\(", src)
         assert m, name
         before = src[max(0, m.start() - 1500):m.start()]
         assert before.rstrip().endswith("*/"), f"{name} has no comment block"
