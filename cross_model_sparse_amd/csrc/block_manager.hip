@@ -341,19 +341,20 @@ namespace {
 // each thread moving 16 pieces, four loads in flight (a tile is H_s * B * B
 // elements, a multiple of 16 bytes for every supported B and dtype).
 constexpr int kSegU4 = 4096;
-__global__ __launch_bounds__(256) void k_pool_store(const uint4* __restrict__ vals, int64_t nnzb,
+typedef unsigned pool_u4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_pool_store(const pool_u4* __restrict__ vals, int64_t nnzb,
                                                     const int32_t* __restrict__ pages,
-                                                    uint4* __restrict__ pool, int64_t n_pages,
+                                                    pool_u4* __restrict__ pool, int64_t n_pages,
                                                     int64_t tile_u4) {
   const int64_t seg0 = (int64_t)blockIdx.x * kSegU4;
   for (int64_t k = blockIdx.y; k < nnzb; k += gridDim.y) {
     const int64_t p = pages[k];
     if (p < 0 || p >= n_pages) continue;
-    const uint4* src = vals + k * tile_u4 + seg0;
-    uint4* dst = pool + p * tile_u4 + seg0;
+    const pool_u4* src = vals + k * tile_u4 + seg0;
+    pool_u4* dst = pool + p * tile_u4 + seg0;
     const int64_t n = tile_u4 - seg0 < kSegU4 ? tile_u4 - seg0 : kSegU4;
     for (int64_t i = threadIdx.x; i < n; i += 4 * 256) {
-      uint4 v[4];
+      pool_u4 v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (i + j * 256 < n) v[j] = src[i + j * 256];
@@ -383,7 +384,7 @@ extern "C" int mf_pool_store(const void* vals, int64_t nnzb, const int32_t* page
   const int64_t tile_u4 = tile_bytes / 16;
   const dim3 grid((unsigned)((tile_u4 + kSegU4 - 1) / kSegU4), (unsigned)std::min<int64_t>(nnzb, 65535));
   hipLaunchKernelGGL(k_pool_store, grid, dim3(256), 0, (hipStream_t)stream,
-                     reinterpret_cast<const uint4*>(vals), nnzb, pages, reinterpret_cast<uint4*>(pool),
+                     reinterpret_cast<const pool_u4*>(vals), nnzb, pages, reinterpret_cast<pool_u4*>(pool),
                      n_pages, tile_u4);
   return mf::hip_check(hipGetLastError(), "k_pool_store launch");
 }

@@ -652,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     lds_barrier();
   }
   int64_t pg_n = 0;                              // table entry of chunk u + NSTG
-  if constexpr (kVar) pg_n = page_raw<kVar>(block_table, col_idx, block_of(NSTG));
+  if constexpr (kVar)
+    if (n_chunks > 0) pg_n = page_raw<kVar>(block_table, col_idx, block_of(NSTG));
   for (int u = 0; u < n_chunks; ++u) {
     // column (and, with a table, page) of chunk u+2: loaded now, combined
     // after this phase's barrier, so neither load waits inside the phase
