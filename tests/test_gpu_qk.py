@@ -53,7 +53,7 @@ def make_inputs(seed, H_s, H_ks, N, d, dt, temp=True):
     return Q, K, scale
 
 
-# name, (H_s, H_ks, N, d, B, dtype, p)
+# name, (H_s, H_ks, N, d, B, dtype, p[, scale multiplier])
 CASES = [
     ("tiny-f32-plain", (4, 4, 200, 64, 16, "f32", 0.9)),
     ("f16-B64-gqa-ragged", (8, 2, 1000, 128, 64, "f16", 0.95)),
@@ -61,14 +61,23 @@ CASES = [
     ("bf16-B128-mqa", (4, 1, 600, 128, 128, "bf16", 0.8)),
     ("f16-B16-plain-mass", (4, 2, 300, 64, 16, "f16", 0.9)),
     ("bf16-short", (2, 1, 40, 128, 32, "bf16", 1.0)),
+    # degenerate cases: one token, fewer tokens than a score tile, a negative
+    # score scale (the log-sum-exp takes its maximum from the smallest
+    # product), a zero scale (every row uniform over its causal keys)
+    ("bf16-one-token", (2, 1, 1, 128, 32, "bf16", 0.9)),
+    ("f16-under-a-tile", (3, 3, 29, 128, 64, "f16", 0.7)),
+    ("f16-negative-scale", (4, 2, 500, 128, 64, "f16", 0.9, -1.0)),
+    ("bf16-zero-scale", (4, 4, 300, 64, 32, "bf16", 0.5, 0.0)),
 ]
 
 
 @pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
 def test_qk_compression_parity(name, cfg):
-    H_s, H_ks, N, d, B, dt, p = cfg
-    say(f"[qk] {name} H_s={H_s} H_ks={H_ks} N={N} d={d} B={B} {dt} p={p}")
+    H_s, H_ks, N, d, B, dt, p = cfg[:7]
+    smul = cfg[7] if len(cfg) > 7 else 1.0
+    say(f"[qk] {name} H_s={H_s} H_ks={H_ks} N={N} d={d} B={B} {dt} p={p} scale x {smul}")
     Q, K, scale = make_inputs(zlib.crc32(name.encode()) % 10000, H_s, H_ks, N, d, dt)
+    scale = scale * smul
     Qh, Kh, sch = host(Q), host(K), scale.double().numpy()
     dev = torch.device("cuda:0")
     Qd, Kd, scd = Q.to(dev), K.to(dev), scale.to(dev)
