@@ -196,17 +196,23 @@ struct KTile {
 // q0 = R0 + 32w .. +31) and split the causal key tiles: half 0 walks tiles
 // [0, nfirst), half 1 tiles [nfirst, nkt), with nfirst a multiple of `align`,
 // so the longest walk is half as long.  K tiles of 32 keys are staged through
-// LDS (two buffers per half; every thread holds its pieces of the next two
-// tiles in registers while the current one is in use).  body(kt, c) receives
-// the tile's raw fp32 products q.k for each wavefront whose rows reach key
-// tile kt; the caller multiplies by the scale (in log2 units).  Workgroups are
-// small enough that several share a CU, at different points of their walks,
-// so one's exponentials overlap another's matrix work.
+// LDS in two buffers per half, loaded from a uniform base with fixed
+// per-thread offsets.
+//
+// Software pipeline: while a wavefront exponentiates the scores of tile kt,
+// it issues the MFMA chain of tile kt+1, one MFMA between each group of
+// exponentials (body(kt, c, mf) must call mf(0) .. mf(NKS-1) once each, in
+// order), so the matrix cores and the vector ALU work at the same time
+// within one wavefront.  At step kt the MFMAs read tile kt+1 from one buffer
+// and tile kt+2 is stored into the other, whose last reader (tile kt) was
+// done before the previous barrier; tile kt+3 is in flight in registers.
+// With `negate` the query operand's signs are flipped, so that a negative
+// score scale becomes a non-negative one on negated products.
 template <bool kBF16, int D, class Body>
 __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
                                         const unsigned short* __restrict__ K, int h, int g,
-                                        int N, int R0, int align, unsigned char* smem,
-                                        Body&& body) {
+                                        int N, int R0, int align, bool negate,
+                                        unsigned char* smem, Body&& body) {
   constexpr int NKS = D / 16;                   // MFMA K steps
   constexpr int kRowU4 = D / 8;                 // 16-byte pieces per row
   constexpr int NP = 32 * kRowU4 / kQkHalf;     // pieces of a tile per thread
@@ -222,8 +228,12 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
   {
     const int row = min(q0 + (lane & 31), N - 1);
     const unsigned short* qr = Q + ((int64_t)h * N + row) * D + 8 * (lane >> 5);
+    const unsigned flip = negate ? 0x80008000u : 0u;   // sign bits of both 16-bit halves
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+    for (int s = 0; s < NKS; ++s) {
+      qop[s] = *reinterpret_cast<const u32x4*>(qr + 16 * s);
+      qop[s] ^= flip;
+    }
   }
   const int last_row = min(N, R0 + kQkRows) - 1;
   const int nkt = last_row / 32 + 1;            // key tiles 0..nkt-1
@@ -259,28 +269,41 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
                                 16 * (pc % kRowU4)) = v[n];
     }
   };
+  // this lane's K operand piece s (row lane%32, chunk 16(lane/32) + 32 s) of buffer b
+  auto read_k = [&](int buf, int s) -> u32x4 {
+    const unsigned char* kb = hs + buf * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
+    return *reinterpret_cast<const u32x4*>(kb + 32 * s);
+  };
   // tile to load for step it of this half (any valid tile once the half is done)
   auto tile_at = [&](int it) { return min(t0 + min(it, max(cnt - 1, 0)), nkt - 1); };
-  // step it: tile t0+it is in LDS buffer BUF, sa holds the next tile (stored
-  // into the other buffer after the compute), the one after is loaded into sb,
-  // so a tile's load has a whole step to land.  Loads are issued on every step
-  // so that the wait before the LDS store counts only the older tile's loads.
-  // Steps alternate the two register sets and buffers: nothing is copied and
-  // LDS offsets are fixed.  Both halves take the same number of barriers.
-  auto step = [&](auto bufc, int it, u32x4* sa, u32x4* sb) {
-    constexpr int BUF = decltype(bufc)::value;
+  // step it (P = it % 2): cur holds the scores of tile t0+it; the MFMAs of
+  // tile t0+it+1 (buffer P^1) go into nxt while body exponentiates cur; sa
+  // holds tile it+2 (stored into buffer P at the end), tile it+3 is loaded
+  // into sb.  Loads are issued on every step so that the wait before the LDS
+  // store counts only the older tile's loads.  Steps alternate register sets
+  // and buffers, so nothing is copied and LDS offsets are fixed; both halves
+  // take the same number of barriers.  The MFMAs of a tile past the half's
+  // end read a valid buffer and are unused.
+  auto step = [&](auto pc, int it, const f32x16& cur, f32x16& nxt, u32x4* sa, u32x4* sb) {
+    constexpr int P = decltype(pc)::value;
     const int kt = t0 + it;
-    load_tile(tile_at(it + 2), sb);
+    load_tile(tile_at(it + 3), sb);
+    // the K operand pieces go through two registers, each read one MFMA ahead
+    u32x4 kc = read_k(P ^ 1, 0);
+    nxt = f32x16{};
+    auto mf = [&](int s) {
+      const u32x4 kn = s + 1 < NKS ? read_k(P ^ 1, s + 1) : kc;
+      nxt = mfma32<kBF16>(kc, qop[s], nxt);
+      kc = kn;
+    };
     if (it < cnt && kt * 32 <= q0 + 31 && q0 < N) {   // some key of the tile is causal for these rows
-      const unsigned char* kb = hs + BUF * KTile<D>::kBytes + (lane & 31) * KTile<D>::kRowBytes + 16 * (lane >> 5);
-      f32x16 c = {};
+      body(kt, cur, mf);
+    } else {
 #pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        c = mfma32<kBF16>(*reinterpret_cast<const u32x4*>(kb + 32 * s), qop[s], c);
-      body(kt, c);
+      for (int s = 0; s < NKS; ++s) mf(s);
     }
     if (it + 1 < nit) {
-      store_tile(BUF ^ 1, sa);
+      store_tile(P, sa);
       __syncthreads();
     }
   };
@@ -288,10 +311,16 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
   load_tile(tile_at(0), stage_a);
   store_tile(0, stage_a);
   load_tile(tile_at(1), stage_a);
+  store_tile(1, stage_a);
+  load_tile(tile_at(2), stage_a);
   __syncthreads();
+  f32x16 ca = {}, cb;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) ca = mfma32<kBF16>(read_k(0, s), qop[s], ca);
+  __syncthreads();                              // buffer 0 is refilled in step 0
   for (int it = 0; it < nit; it += 2) {
-    step(std::integral_constant<int, 0>{}, it, stage_a, stage_b);
-    if (it + 1 < nit) step(std::integral_constant<int, 1>{}, it + 1, stage_b, stage_a);
+    step(std::integral_constant<int, 0>{}, it, ca, cb, stage_a, stage_b);
+    if (it + 1 < nit) step(std::integral_constant<int, 1>{}, it + 1, cb, ca, stage_b, stage_a);
   }
 }
 
@@ -314,41 +343,53 @@ __device__ __forceinline__ void qk_item(int ngrp, int H_s, int& h, int& grp) {
 // key of output element e of this lane within a tile
 __device__ __forceinline__ int tile_key(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 
+// The MFMA calls and exponential groups of a fully causal tile alternate as
+// written: sched_barrier keeps the compiler from gathering the MFMAs.
+#define MF_PIN() __builtin_amdgcn_sched_barrier(0)
+
 template <bool kBF16, int D>
-__global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
+__global__ __launch_bounds__(kQkThreads, 4) void k_lse_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
     int H_ks, int N, const float* __restrict__ scale, float* __restrict__ lse) {
+  constexpr int NKS = D / 16;
+  constexpr int EPS = 16 / NKS;                  // scores per MFMA step
   __shared__ __align__(16) unsigned char smem[4 * KTile<D>::kBytes];
   __shared__ float2 half1[kQkRows];              // (max, sum) of half 1 per row
   const int ngrp = (N + kQkRows - 1) / kQkRows;
   int h, grp;
   qk_item(ngrp, H_s, h, grp);
   const int g = h / (H_s / H_ks);
-  const float sc = scale[h] * kLog2e;
+  const float sc_raw = scale[h] * kLog2e;
+  const bool neg = sc_raw < 0.f;                 // products negated by the walk
+  const float sc = fabsf(sc_raw);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int R0 = grp * kQkRows;
   const int q0 = R0 + 32 * (wave % kQkHalfWaves);
   const int row = q0 + (lane & 31);
   float m = -INFINITY, l = 0.f;                  // running maximum and sum, log2 units
-  qk_walk<kBF16, D>(Q, K, h, g, N, R0, 1, smem, [&](int kt, const f32x16& c) {
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, 1, neg, smem, [&](int kt, const f32x16& c, auto&& mf) {
     if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
-      // the maximum of sc * c is sc times the maximum (sc >= 0) or minimum of c
+      // sc >= 0: the maximum of sc * c is sc times the maximum of c
       float r = c[0];
-      if (sc >= 0.f) {
 #pragma unroll
-        for (int e = 1; e < 16; ++e) r = fmaxf(r, c[e]);
-      } else {
-#pragma unroll
-        for (int e = 1; e < 16; ++e) r = fminf(r, c[e]);
-      }
+      for (int e = 1; e < 16; ++e) r = fmaxf(r, c[e]);
       const float mx = fmaxf(m, r * sc);
       float s = l * exp2_sum(m - mx);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += exp2_sum(fmaf(c[e], sc, -mx));
+      for (int k = 0; k < NKS; ++k) {
+        MF_PIN();
+        mf(k);
+        MF_PIN();
+#pragma unroll
+        for (int e = k * EPS; e < (k + 1) * EPS; ++e) s += exp2_sum(fmaf(c[e], sc, -mx));
+      }
+      MF_PIN();
       l = s;
       m = mx;
     } else {
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) mf(k);
       float x[16];
       float mx = m;
 #pragma unroll
@@ -385,10 +426,12 @@ __global__ __launch_bounds__(kQkThreads) void k_lse_mfma(
 }
 
 template <bool kBF16, int D>
-__global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
+__global__ __launch_bounds__(kQkThreads, 4) void k_mass_qk_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
     int H_ks, int N, int B, const float* __restrict__ scale, const float* __restrict__ lse,
     float* __restrict__ part) {
+  constexpr int NKS = D / 16;
+  constexpr int EPS = 16 / NKS;                  // scores per MFMA step
   __shared__ __align__(16) unsigned char smem[4 * KTile<D>::kBytes];
   const int T = (N + B - 1) / B;
   const int NRT = (N + kRT - 1) / kRT;
@@ -396,45 +439,56 @@ __global__ __launch_bounds__(kQkThreads) void k_mass_qk_mfma(
   int h, grp;
   qk_item(ngrp, H_s, h, grp);
   const int g = h / (H_s / H_ks);
-  const float sc = scale[h] * kLog2e;
+  const float sc_raw = scale[h] * kLog2e;
+  const bool neg = sc_raw < 0.f;                 // products negated by the walk
+  const float sc = fabsf(sc_raw);
   const int lane = threadIdx.x & 63;
   const int tpb = B / 32;                        // key tiles per column block
-  {
-    const int R0 = grp * kQkRows;
-    const int q0 = R0 + 32 * ((threadIdx.x >> 6) % kQkHalfWaves);
-    const int row = q0 + (lane & 31);
-    const float l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
-    float acc = 0.f;
-    // sums of the lanes of one 16-row tile: lanes {0..15, 32..47} and {16..31, 48..63}
-    auto flush = [&](int J) {
-      float v = acc;
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 32);
-      const int rt = q0 / kRT + ((lane >> 4) & 1);
-      if ((lane == 0 || lane == 16) && rt * kRT < N) part[((int64_t)h * NRT + rt) * T + J] = v;
-      acc = 0.f;
-    };
-    // halves split at a column-block boundary: each block's partials come from one half
-    qk_walk<kBF16, D>(Q, K, h, g, N, R0, tpb, smem, [&](int kt, const f32x16& c) {
-      if (kt * 32 + 31 <= q0 && q0 + 31 < N) {  // every key of the tile is causal for every row
+  const int R0 = grp * kQkRows;
+  const int q0 = R0 + 32 * ((threadIdx.x >> 6) % kQkHalfWaves);
+  const int row = q0 + (lane & 31);
+  const float l2 = row < N ? lse[(int64_t)h * N + row] * kLog2e : 0.f;
+  float acc = 0.f;
+  // sums of the lanes of one 16-row tile: lanes {0..15, 32..47} and {16..31, 48..63}
+  auto flush = [&](int J) {
+    float v = acc;
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 32);
+    const int rt = q0 / kRT + ((lane >> 4) & 1);
+    if ((lane == 0 || lane == 16) && rt * kRT < N) part[((int64_t)h * NRT + rt) * T + J] = v;
+    acc = 0.f;
+  };
+  // halves split at a column-block boundary: each block's partials come from one half
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, tpb, neg, smem, [&](int kt, const f32x16& c, auto&& mf) {
+    if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc += exp2_sum(fmaf(c[e], sc, -l2));
-      } else {
+      for (int k = 0; k < NKS; ++k) {
+        MF_PIN();
+        mf(k);
+        MF_PIN();
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int j = kt * 32 + tile_key(lane, e);
-          acc += (j <= row && j < N && row < N) ? exp2_sum(fmaf(c[e], sc, -l2)) : 0.f;
-        }
+        for (int e = k * EPS; e < (k + 1) * EPS; ++e) acc += exp2_sum(fmaf(c[e], sc, -l2));
       }
-      const int J = kt / tpb;
-      // the block's last tile, or the last tile these rows reach
-      if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) flush(J);
-    });
-  }
+      MF_PIN();
+    } else {
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) mf(k);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = kt * 32 + tile_key(lane, e);
+        acc += (j <= row && j < N && row < N) ? exp2_sum(fmaf(c[e], sc, -l2)) : 0.f;
+      }
+    }
+    const int J = kt / tpb;
+    // the block's last tile, or the last tile these rows reach
+    if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) flush(J);
+  });
 }
+
+#undef MF_PIN
 
 // two values rounded to the storage type (RNE), packed low first
 template <bool kBF16>
