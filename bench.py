@@ -131,6 +131,7 @@ def main():
         x.update(mass=mass, rp=rp, ci=ci, vals=vals, nnzb=nnzb,
                  ws=torch.empty(mf.topp_workspace_bytes(N, B), dtype=torch.uint8, device=dev),
                  O=torch.empty(N, w.H_r, w.d, dtype=synth.torch_dtype(w.dtype), device=dev))
+    ws_bm = torch.empty(max(1, mf.block_mass_ws_bytes(w.H_s, N, B)), dtype=torch.uint8, device=dev)
     ws_r = torch.empty(max(1, mf.retrieve_workspace_bytes(N, B, w.H_kv, w.d,
                                                           synth.torch_dtype(w.dtype))),
                        dtype=torch.uint8, device=dev)
@@ -156,7 +157,7 @@ def main():
         for x in layers:
             e0, e1, e2, e3 = ev(), ev(), ev(), ev()
             if record: e0.record(stream)
-            mf.block_mass(x["A"], B, out=x["mass"])
+            mf.block_mass(x["A"], B, out=x["mass"], workspace=ws_bm)
             if record: e1.record(stream)
             mf.topp_select_bsr(x["mass"], x["A"], B, w.p, cap_nnzb=x["nnzb"],
                                row_ptr=x["rp"], col_idx=x["ci"], vals=x["vals"],

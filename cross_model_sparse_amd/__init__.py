@@ -5,7 +5,7 @@ include/mapflow.h); :mod:`cross_model_sparse_amd.mapflow` is its thin Python
 binding over torch device tensors.
 """
 from .mapflow import (  # noqa: F401
-    MapflowError, CapacityError, abi_version, block_mass, topp_select_bsr,
+    MapflowError, CapacityError, abi_version, block_mass, block_mass_ws_bytes, topp_select_bsr,
     retrieve_fused, retrieve_fused_multi, retrieve_fused_varlen, retrieve_kernel, compress, topp_workspace_bytes, retrieve_workspace_bytes, load, lib_path, EXPORTED,
     row_lse, block_mass_qk, block_mass_qk_workspace_bytes, topp_select_bsr_qk, compress_qk,
     BlockManager, prefix_hashes, pool_store,

@@ -106,9 +106,179 @@ hipError_t launch_t(const void* A, int H_s, int N, int B, float* mass,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Row-streaming variant (needs a workspace)
+// ---------------------------------------------------------------------------
+//
+// A workgroup owns one (head h, block row I): it streams the causal part of
+// the block row's map rows, columns [0, min(N, (I+1)B)), as whole contiguous
+// rows (a scan of the map in column strips reads 1 KB pieces of rows N*e
+// bytes apart and reaches about 80% of the rate of whole rows).  Columns go in
+// chunks of at most NPT * kRowThreads 16-byte pieces; within a chunk every
+// thread owns NPT fixed pieces (so fixed column blocks) of RPP rows per pass,
+// sums their elements in fp32 and accumulates in fp64, with UNR rows in
+// flight.  Each chunk's per-J totals are formed over LDS in a fixed order and
+// stored, once rounded to fp32, as part[h][I(I+1)/2 + J] (the causal
+// triangle); a second kernel adds the heads in a fixed order in fp64.
+// Workgroups go longest row first, consecutive ones on different heads of the
+// same block row.
+constexpr int kRowThreads = 512;
+
+template <class TT, int VEC, int UNR>
+__global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
+    const typename TT::S* __restrict__ A, int H_s, int N, int B, float* __restrict__ part) {
+  using S = typename TT::S;
+  using V = typename VecT<VEC>::T;
+  constexpr int EPV = VEC / (int)sizeof(S);      // elements per piece
+  constexpr int NPT = 2;                         // pieces per thread in a wide chunk
+  __shared__ double red[NPT * kRowThreads];
+  const int T = (N + B - 1) / B;
+  const int h = blockIdx.x % H_s;
+  const int I = T - 1 - (int)(blockIdx.x / H_s);
+  const int tid = threadIdx.x;
+  const int rows = min(B, N - I * B);
+  const int cols = min(N, (I + 1) * B);          // causal columns of these rows
+  const int P = cols / EPV;                      // pieces per row (cols is a multiple of EPV)
+  const int CPJ = B / EPV;                       // pieces per column block
+  const int64_t tri = (int64_t)T * (T + 1) / 2;
+  float* out = part + (int64_t)h * tri + (int64_t)I * (I + 1) / 2;
+  const S* rowbase = A + ((int64_t)h * N + (int64_t)I * B) * N;
+  for (int c0 = 0; c0 < P; c0 += NPT * kRowThreads) {
+    const int CW = min(P - c0, NPT * kRowThreads);  // pieces in this chunk
+    // narrow chunk (CW <= kRowThreads): one piece per thread, RPP rows per
+    // pass; wide chunk: pieces c and c + kRowThreads of every row (the second
+    // clamped into the chunk and masked, so that both loads are unconditional)
+    const int W = min(CW, kRowThreads);
+    const int RPP = kRowThreads / W;             // rows per pass
+    const int rr = tid / W, c = tid % W;
+    double acc0 = 0.0, acc1 = 0.0;
+    if (CW <= kRowThreads) {
+      if (rr < RPP) {
+        const S* p = rowbase + (int64_t)rr * N + (int64_t)(c0 + c) * EPV;
+        const int64_t step = (int64_t)RPP * N;
+        int r = rr;
+        for (; r + (UNR - 1) * RPP < rows; r += UNR * RPP) {
+          V v[UNR];
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) v[u] = *reinterpret_cast<const V*>(p + u * step);
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) acc0 += (double)vec_sum<TT, VEC>(v[u]);
+          p += UNR * step;
+        }
+        for (; r < rows; r += RPP, p += step) acc0 += (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p));
+      }
+    } else {
+      const bool has1 = c + kRowThreads < CW;
+      const int c1 = has1 ? c + kRowThreads : CW - 1;
+      const S* p0 = rowbase + (int64_t)(c0 + c) * EPV;
+      const S* p1 = rowbase + (int64_t)(c0 + c1) * EPV;
+      constexpr int U2 = UNR / 2;
+      int r = 0;
+      for (; r + U2 - 1 < rows; r += U2) {
+        V v0[U2], v1[U2];
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+          v0[u] = *reinterpret_cast<const V*>(p0 + (int64_t)(r + u) * N);
+          v1[u] = *reinterpret_cast<const V*>(p1 + (int64_t)(r + u) * N);
+        }
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+          acc0 += (double)vec_sum<TT, VEC>(v0[u]);
+          const double s1 = (double)vec_sum<TT, VEC>(v1[u]);
+          acc1 += has1 ? s1 : 0.0;
+        }
+      }
+      for (; r < rows; ++r) {
+        acc0 += (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p0 + (int64_t)r * N));
+        const double s1 = (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p1 + (int64_t)r * N));
+        acc1 += has1 ? s1 : 0.0;
+      }
+    }
+    red[tid] = acc0;
+    red[kRowThreads + tid] = acc1;
+    __syncthreads();
+    // column blocks of this chunk, J = (c0 + x) / CPJ for x < CW; piece x is
+    // held by threads (x % W) + W q, q < RPP, in slot k = x / W.  Chunks start
+    // at multiples of NPT * kRowThreads, which CPJ (a power of two <= 128)
+    // divides, so no column block spans two chunks.
+    const int j0 = c0 / CPJ, j1 = (c0 + CW - 1) / CPJ;
+    for (int jj = tid; jj <= j1 - j0; jj += kRowThreads) {
+      const int J = j0 + jj;
+      const int xb = J * CPJ - c0, xe = min((J + 1) * CPJ, c0 + CW) - c0;
+      double s = 0.0;
+      for (int x = xb; x < xe; ++x) {
+        const int k = x / W, cc = x - k * W;
+        for (int q = 0; q < RPP; ++q) s += red[k * kRowThreads + q * W + cc];
+      }
+      out[J] = (float)s;
+    }
+    __syncthreads();
+  }
+}
+
+// mass[I][J] = (1/H_s) sum_h part[h][I(I+1)/2 + J] in fp64, head order fixed;
+// J > I is 0.  Workgroup (I, 64 columns); thread (column, head group q of 4)
+// adds heads q, q+4, ...; the four partials are added in the order 0..3.
+__global__ __launch_bounds__(256) void k_block_mass_heads(const float* __restrict__ part, int H_s,
+                                                          int T, float* __restrict__ mass) {
+  __shared__ double red[4][64];
+  const int I = blockIdx.y;
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int J = blockIdx.x * 64 + c;
+  const int64_t tri = (int64_t)T * (T + 1) / 2;
+  const int64_t o = (int64_t)I * (I + 1) / 2 + J;
+  double s = 0.0;
+  if (J <= I)
+    for (int h = q; h < H_s; h += 4) s += (double)part[(int64_t)h * tri + o];
+  red[q][c] = s;
+  __syncthreads();
+  if (q == 0 && J < T)
+    mass[(int64_t)I * T + J] = J <= I ? (float)((((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]) / (double)H_s) : 0.f;
+}
+
+template <class TT, int VEC>
+hipError_t launch_rows_t(const void* A, int H_s, int N, int B, float* mass, float* part,
+                         hipStream_t st) {
+  const int T = mf::blocks_of(N, B);
+  const auto* a = reinterpret_cast<const typename TT::S*>(A);
+  hipLaunchKernelGGL((k_block_mass_rows<TT, VEC, 8>), dim3(H_s * T), dim3(kRowThreads), 0, st,
+                     a, H_s, N, B, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_block_mass_heads, dim3((T + 63) / 64, T), dim3(256), 0, st, part, H_s, T, mass);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace mf {
+
+size_t block_mass_rows_workspace_bytes(int H_s, int N, int B) {
+  const int64_t T = blocks_of(N, B);
+  return (size_t)H_s * (size_t)(T * (T + 1) / 2) * sizeof(float);
+}
+
+hipError_t launch_block_mass_rows(const void* A, int dt, int H_s, int N, int B, float* mass,
+                                  void* workspace, hipStream_t st) {
+  float* part = reinterpret_cast<float*>(workspace);
+  const int esz = dtype_bytes(dt);
+  const int vec = row_vec_bytes(A, N, B, esz);
+  if (dt == MF_F32) {
+    if (vec >= 16) return launch_rows_t<mfd::TF32, 16>(A, H_s, N, B, mass, part, st);
+    if (vec >= 8) return launch_rows_t<mfd::TF32, 8>(A, H_s, N, B, mass, part, st);
+    return launch_rows_t<mfd::TF32, 4>(A, H_s, N, B, mass, part, st);
+  }
+  if (dt == MF_F16) {
+    if (vec >= 16) return launch_rows_t<mfd::TF16, 16>(A, H_s, N, B, mass, part, st);
+    if (vec >= 8) return launch_rows_t<mfd::TF16, 8>(A, H_s, N, B, mass, part, st);
+    if (vec >= 4) return launch_rows_t<mfd::TF16, 4>(A, H_s, N, B, mass, part, st);
+    return launch_rows_t<mfd::TF16, 2>(A, H_s, N, B, mass, part, st);
+  }
+  if (vec >= 16) return launch_rows_t<mfd::TBF16, 16>(A, H_s, N, B, mass, part, st);
+  if (vec >= 8) return launch_rows_t<mfd::TBF16, 8>(A, H_s, N, B, mass, part, st);
+  if (vec >= 4) return launch_rows_t<mfd::TBF16, 4>(A, H_s, N, B, mass, part, st);
+  return launch_rows_t<mfd::TBF16, 2>(A, H_s, N, B, mass, part, st);
+}
 
 hipError_t launch_block_mass(const void* A, int dt, int H_s, int N, int B,
                              float* mass, hipStream_t st) {

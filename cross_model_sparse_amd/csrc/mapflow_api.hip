@@ -76,6 +76,26 @@ const char* mf_status_string(int status) {
 
 const char* mf_last_error(void) { return mf::g_last_error.c_str(); }
 
+size_t mf_block_mass_ws_bytes(int H_s, int N, int B) {
+  if (H_s < 1 || N < 1 || B < 1) return 0;
+  return mf::block_mass_rows_workspace_bytes(H_s, N, B);
+}
+
+int mf_block_mass_ws(const void* A, int dtype, int H_s, int N, int B, float* mass,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mf_block_mass_ws";
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (!A || !mass || !workspace) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  const size_t need = mf::block_mass_rows_workspace_bytes(H_s, N, B);
+  if (workspace_bytes < need)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          (long long)workspace_bytes, (long long)need));
+  return mf::hip_check(mf::launch_block_mass_rows(A, dtype, H_s, N, B, mass, workspace,
+                                                  (hipStream_t)stream),
+                       "mf_block_mass_ws launch");
+}
+
 int mf_block_mass(const void* A, int dtype, int H_s, int N, int B, float* mass,
                   void* stream) {
   int st = check_geom("mf_block_mass", dtype, H_s, N, B);

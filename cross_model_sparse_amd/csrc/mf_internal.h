@@ -22,6 +22,11 @@ inline int dtype_bytes(int dt) { return dt == MF_F32 ? 4 : 2; }
 int row_vec_bytes(const void* base, int N, int B, int esize);
 
 // Kernel launchers (one per translation unit); arguments already validated.
+// Row-streaming block mass: per-(head, block row) workgroups into an fp32
+// workspace of block_mass_rows_workspace_bytes, then a fixed-order head sum.
+size_t block_mass_rows_workspace_bytes(int H_s, int N, int B);
+hipError_t launch_block_mass_rows(const void* A, int dt, int H_s, int N, int B, float* mass,
+                                  void* workspace, hipStream_t st);
 hipError_t launch_block_mass(const void* A, int dt, int H_s, int N, int B,
                              float* mass, hipStream_t st);
 hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,

@@ -23,6 +23,7 @@ MF_F32, MF_F16, MF_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_BF16}
 
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
+            "mf_block_mass_ws_bytes", "mf_block_mass_ws",
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
             "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
@@ -117,6 +118,10 @@ def load() -> ctypes.CDLL:
     L.mf_bm_stats.argtypes = [c_vp, c_vp]
     L.mf_pool_store.restype = c_int
     L.mf_pool_store.argtypes = [c_vp, c_i64, c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp]
+    L.mf_block_mass_ws_bytes.restype = c_sz
+    L.mf_block_mass_ws_bytes.argtypes = [c_int, c_int, c_int]
+    L.mf_block_mass_ws.restype = c_int
+    L.mf_block_mass_ws.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp, c_sz, c_vp]
     L.mf_retrieve_fused_varlen.restype = c_int
     L.mf_retrieve_fused_varlen.argtypes = [c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_i64, c_i64, c_int, c_int, c_int, c_vp, c_int,
@@ -170,9 +175,18 @@ def retrieve_workspace_bytes(N: int, B: int, H_kv: int, d: int, dtype: torch.dty
     return int(load().mf_retrieve_workspace_bytes(N, B, H_kv, d, _DTYPE_CODE[dtype]))
 
 
+def block_mass_ws_bytes(H_s: int, N: int, B: int) -> int:
+    return int(load().mf_block_mass_ws_bytes(H_s, N, B))
+
+
 def block_mass(A: torch.Tensor, B: int, out: torch.Tensor | None = None,
-               stream=None) -> torch.Tensor:
-    """mass[T][T] fp32 of a contiguous [H_s][N][N] sender map (mf_block_mass)."""
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mass[T][T] fp32 of a contiguous [H_s][N][N] sender map.
+
+    With a workspace (a uint8 device tensor of at least block_mass_ws_bytes)
+    the row-streaming kernels run (mf_block_mass_ws); with workspace=False the
+    allocation-free column-strip scan (mf_block_mass); by default a workspace
+    is allocated."""
     _need_cuda(A)
     H_s, N, N2 = A.shape
     if N2 != N or not A.is_contiguous():
@@ -180,7 +194,14 @@ def block_mass(A: torch.Tensor, B: int, out: torch.Tensor | None = None,
     T = -(-N // B)
     if out is None:
         out = torch.empty(T, T, dtype=torch.float32, device=A.device)
-    _check(load().mf_block_mass(_ptr(A), _dcode(A), H_s, N, B, _ptr(out), _stream(stream)))
+    if workspace is False:
+        _check(load().mf_block_mass(_ptr(A), _dcode(A), H_s, N, B, _ptr(out), _stream(stream)))
+        return out
+    if workspace is None:
+        workspace = torch.empty(max(1, block_mass_ws_bytes(H_s, N, B)), dtype=torch.uint8,
+                                device=A.device)
+    _check(load().mf_block_mass_ws(_ptr(A), _dcode(A), H_s, N, B, _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -87,6 +87,24 @@ const char* mf_last_error(void);
 int mf_block_mass(const void* A, int dtype, int H_s, int N, int B,
                   float* mass, void* stream);
 
+/* Workspace bytes of mf_block_mass_ws: H_s * T(T+1)/2 float32 (0 for bad sizes). */
+size_t mf_block_mass_ws_bytes(int H_s, int N, int B);
+
+/*
+ * The same block masses as mf_block_mass (same statistic, same masses up to
+ * the order of the fp64 additions; bit-reproducible run to run), computed by
+ * streaming whole map rows: one workgroup per (head, block row) reads the
+ * causal part of that block row's rows as contiguous runs and leaves its
+ * per-tile sums, rounded once to fp32, in `workspace`; a second kernel adds
+ * the heads in a fixed order in fp64 and divides by H_s.  Faster than the
+ * column-strip scan of mf_block_mass, at the price of a caller-owned device
+ * workspace of at least mf_block_mass_ws_bytes(H_s, N, B) bytes (overwritten).
+ *  Errors: those of mf_block_mass, plus MF_ERR_INVALID for a null or short
+ *  workspace.
+ */
+int mf_block_mass_ws(const void* A, int dtype, int H_s, int N, int B, float* mass,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes mf_topp_select_bsr needs for (N, B). */
 size_t mf_topp_workspace_bytes(int N, int B);
 

@@ -324,3 +324,17 @@ def _multi(L, n=2, **kw):
 def test_retrieve_multi_rejects(L, n, kw, frag):
     assert _multi(L, n, **kw) == mf.MF_ERR_INVALID
     assert frag in _last(L)
+
+
+# ---- row-streaming block mass ----------------------------------------------------
+
+def test_block_mass_ws_size_and_rejects(L):
+    assert L.mf_block_mass_ws_bytes(40, 8192, 64) == 40 * 128 * 129 // 2 * 4
+    assert L.mf_block_mass_ws_bytes(0, 8192, 64) == 0
+    args = (FAKE, 2, 40, 8192, 64, FAKE)
+    need = L.mf_block_mass_ws_bytes(40, 8192, 64)
+    assert L.mf_block_mass_ws(*args, None, need, None) == mf.MF_ERR_INVALID
+    assert "null" in _last(L)
+    assert L.mf_block_mass_ws(*args, FAKE, need - 1, None) == mf.MF_ERR_INVALID
+    assert "workspace" in _last(L)
+    assert L.mf_block_mass_ws(FAKE, 2, 40, 8192, 48, FAKE, FAKE, need, None) == mf.MF_ERR_INVALID

@@ -364,3 +364,24 @@ def test_full_varlen_sequences(gpu):
             w = w0.with_(N=n)
             run_end_to_end(w, gpu, rows=_sample_rows(w.T, extra=2, seed=i), p=p,
                            seed=5000 + lens.index(n))
+
+
+@pytest.mark.parametrize("name,ov", [("pair14b8b-bf16", dict(N=1111)), ("tiny-f32", dict(N=250)),
+                                     ("pair8b3b-f16", dict(N=700, B=32))])
+def test_block_mass_variants_agree(gpu, name, ov):
+    # the row-streaming kernels (workspace) and the column-strip scan compute the
+    # same statistic; both against the oracle, each bit-reproducible
+    w = synth.workload(name, **ov)
+    L = synth.gen_layer(w, device=gpu)
+    A = L["A"]
+    m_ws = mf.block_mass(A, w.B)
+    m_ws2 = mf.block_mass(A, w.B)
+    m_strip = mf.block_mass(A, w.B, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(m_ws, m_ws2)
+    ref = oracle.block_mass(HostView(A), w.B)
+    for m in (host(m_ws), host(m_strip)):
+        tri = np.tril_indices(w.T)
+        rel = np.abs(m[tri] - ref[tri]) / np.maximum(np.abs(ref[tri]), 1e-30)
+        assert rel.max() <= 1e-6, rel.max()
+        assert np.all(np.triu(m, 1) == 0)
