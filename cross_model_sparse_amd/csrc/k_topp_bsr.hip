@@ -7,12 +7,14 @@
 // (article aitest123.com/news/zaoi86, third section, second component).
 //
 // Three launches on the caller's stream:
-//  1. k_select  one workgroup per block row: bitonic sort of the row's causal
-//               candidates in LDS by (mass descending, column ascending), then
-//               a single-lane fp64 walk (row total in column order, running
+//  1. k_select  one workgroup per block row: sort of the row's causal
+//               candidates in LDS by (mass descending, column ascending) (rank
+//               counting up to 512 candidates, a bitonic network above), then
+//               a single-lane fp64 walk over the masses staged in LDS (row total in column order, running
 //               sum in sorted order) that stops at the first running sum
-//               >= p * total, then an LDS compaction of the kept columns into
-//               ascending order.  Sequential sums keep the decision exactly
+//               >= p * total, then a compaction of the kept columns into
+//               ascending order (wavefront ballots up to 256 candidates, an
+//               LDS scan above).  Sequential sums keep the decision exactly
 //               reproducible and independent of the launch shape.
 //  2. k_scan    one workgroup: exclusive scan of the per-row counts -> row_ptr.
 //  3. k_gather  grid-stride over (kept block, group of 8 heads): writes
@@ -42,6 +44,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* __restrict__ mass, int T, float p, int32_t* __restrict__ kept,
     int32_t* __restrict__ count) {
   __shared__ unsigned long long keys[kMaxT];
+  __shared__ float mv[kMaxT];                    // the row's masses, for the fp64 walk
   __shared__ unsigned char flag[kMaxT];
   __shared__ int scan_buf[kSelThreads];
   __shared__ int k_sh;
@@ -58,35 +61,58 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
   int n = 1;
   while (n < ncand) n <<= 1;
   for (int j = tid; j < n; j += kSelThreads) {
-    keys[j] = (j < ncand) ? desc_key(mrow[j], j) : ~0ull;
-    if (j < ncand) flag[j] = 0;
+    const float m = j < ncand ? mrow[j] : 0.f;
+    keys[j] = (j < ncand) ? desc_key(m, j) : ~0ull;
+    if (j < ncand) {
+      mv[j] = m;
+      flag[j] = 0;
+    }
   }
   __syncthreads();
-  // Bitonic sort, ascending keys.
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (n >> 1); t += kSelThreads) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        unsigned long long a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
+  if (ncand <= 2 * kSelThreads) {
+    // Rank sort, ascending keys: keys are distinct (the column is in the low
+    // bits), so the number of smaller keys is each key's sorted position; no
+    // barrier between steps, unlike the bitonic network below.
+    const bool h0 = tid < ncand, h1 = tid + kSelThreads < ncand;
+    const unsigned long long k0 = h0 ? keys[tid] : 0ull;
+    const unsigned long long k1 = h1 ? keys[tid + kSelThreads] : 0ull;
+    int r0 = 0, r1 = 0;
+    for (int i = 0; i < ncand; ++i) {
+      const unsigned long long ki = keys[i];
+      r0 += ki < k0;
+      r1 += ki < k1;
+    }
+    __syncthreads();
+    if (h0) keys[r0] = k0;
+    if (h1) keys[r1] = k1;
+    __syncthreads();
+  } else {
+    // Bitonic sort, ascending keys.
+    for (int size = 2; size <= n; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < (n >> 1); t += kSelThreads) {
+          const int lo = 2 * t - (t & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = ((lo & size) == 0);
+          unsigned long long a = keys[lo], b = keys[hi];
+          if ((a > b) == up) {
+            keys[lo] = b;
+            keys[hi] = a;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   if (tid == 0) {
     double total = 0.0;
-    for (int J = 0; J < ncand; ++J) total += (double)mrow[J];
+    for (int J = 0; J < ncand; ++J) total += (double)mv[J];
     const double thr = (double)p * total;
     double cum = 0.0;
     int k = 0;
     while (k < ncand) {
       const int J = (int)(keys[k] & 0xffffffffu);
-      cum += (double)mrow[J];
+      cum += (double)mv[J];
       flag[J] = 1;
       ++k;
       if (cum >= thr) break;
@@ -95,6 +121,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
   }
   __syncthreads();
   // Compact flagged columns in ascending order.
+  if (ncand <= kSelThreads) {
+    // one candidate per thread: position = kept columns below it, counted by
+    // wavefront ballots
+    const bool f = tid < ncand && flag[tid];
+    const unsigned long long b = __ballot(f);
+    const int lane = tid & 63, w = tid >> 6;
+    if (lane == 0) scan_buf[w] = __popcll(b);
+    __syncthreads();
+    int pos = __popcll(b & ((1ull << lane) - 1ull));
+    for (int q = 0; q < w; ++q) pos += scan_buf[q];
+    if (f) kept[(int64_t)I * T + pos] = tid;
+    if (tid == 0) count[I] = k_sh;
+    return;
+  }
   const int chunk = (ncand + kSelThreads - 1) / kSelThreads;
   const int j0 = tid * chunk, j1 = min(ncand, j0 + chunk);
   int c = 0;
@@ -113,7 +153,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
   if (tid == 0) count[I] = k_sh;
 }
 
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;
 
 __global__ __launch_bounds__(kScanThreads) void k_scan(
     const int32_t* __restrict__ count, int T, int32_t* __restrict__ row_ptr) {
