@@ -338,8 +338,10 @@ namespace {
 
 // pool[pages[k]] = vals[k] for every k with pages[k] in [0, n_pages).
 // Workgroup (segment, block k): 64 KB of the tile (4096 pieces of 16 bytes),
-// each thread moving 16 pieces, four loads in flight (a tile is H_s * B * B
-// elements, a multiple of 16 bytes for every supported B and dtype).
+// each thread moving 16 pieces; a whole segment issues all 16 loads
+// unconditionally before its stores, a partial last segment goes four at a
+// time under bounds checks (a tile is H_s * B * B elements, a multiple of 16
+// bytes for every supported B and dtype).
 constexpr int kSegU4 = 4096;
 typedef unsigned pool_u4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void k_pool_store(const pool_u4* __restrict__ vals, int64_t nnzb,
@@ -353,6 +355,16 @@ __global__ __launch_bounds__(256) void k_pool_store(const pool_u4* __restrict__ 
     const pool_u4* src = vals + k * tile_u4 + seg0;
     pool_u4* dst = pool + p * tile_u4 + seg0;
     const int64_t n = tile_u4 - seg0 < kSegU4 ? tile_u4 - seg0 : kSegU4;
+    if (n == kSegU4) {
+      // whole segment: every load unconditional, all 16 in flight at once
+      constexpr int kPer = kSegU4 / 256;
+      pool_u4 v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) v[j] = src[threadIdx.x + j * 256];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) dst[threadIdx.x + j * 256] = v[j];
+      continue;
+    }
     for (int64_t i = threadIdx.x; i < n; i += 4 * 256) {
       pool_u4 v[4];
 #pragma unroll
