@@ -478,7 +478,8 @@ def varlen_leg(dev, reps):
     """The packed varlen batch: 16 sequences, lengths U[1024, 16384] (seeded),
     B = 64, H_s = 32, H_r = 24, H_kv = 8, d = 128, bf16, p = 0.9, structured
     maps.  Each sequence's dense map is generated, compressed (block mass +
-    Top-p/BSR, HIP events) and freed in turn; the kept tiles of all sequences
+    Top-p/BSR into buffers allocated once for the longest sequence, HIP
+    events) and freed in turn; the kept tiles of all sequences
     then sit in one pool in a shuffled page order.  Timed with HIP events
     (medians over `reps`): the whole batch's retrieval in one launch through
     the block table, the same over a contiguous pool without a table, and one
@@ -491,24 +492,39 @@ def varlen_leg(dev, reps):
     B, p, e = w0.B, w0.p, synth.DTYPE_BYTES[w0.dtype]
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    # compression buffers sized once for the longest sequence, as a serving
+    # loop holds them: workspaces, masses and a BSR of full causal capacity
+    Tm = -(-max(lens) // B)
+    cap_m = Tm * (Tm + 1) // 2
+    ws_bm = torch.empty(mf.block_mass_ws_bytes(w0.H_s, max(lens), B), dtype=torch.uint8, device=dev)
+    ws_tp = torch.empty(mf.topp_workspace_bytes(max(lens), B), dtype=torch.uint8, device=dev)
+    mass_b = torch.empty(Tm * Tm, dtype=torch.float32, device=dev)
+    rp_b = torch.empty(Tm + 1, dtype=torch.int32, device=dev)
+    ci_b = torch.empty(cap_m, dtype=torch.int32, device=dev)
+    vals_b = torch.empty(cap_m, w0.H_s, B, B, dtype=synth.torch_dtype(w0.dtype), device=dev)
     seqs, W, t_comp = [], None, 0.0
     for s, n in enumerate(lens):
         g = synth.gen_layer(w0.with_(N=n), device=dev, seed=5000 + s)
         if W is None:
             W = g["W"].to(dev)
         A = g["A"]
+        T = -(-n // B)
+        mass = mass_b[: T * T].view(T, T)
         torch.cuda.synchronize()
         a, b = ev(), ev()
         a.record(stream)
-        mass = mf.block_mass(A, B)
-        rp, ci, vals, nnzb = mf.topp_select_bsr(mass, A, B, p)   # reads nnzb: one sync
+        mf.block_mass(A, B, out=mass, workspace=ws_bm)
+        mf.topp_select_bsr(mass, A, B, p, cap_nnzb=T * (T + 1) // 2, row_ptr=rp_b[: T + 1],
+                           col_idx=ci_b, vals=vals_b, workspace=ws_tp, sync=False)
         b.record(stream)
         b.synchronize()
         t_comp += a.elapsed_time(b)
-        seqs.append(dict(N=n, rp=rp, ci=ci[:nnzb], vals=vals[:nnzb].clone(), nnzb=nnzb,
-                         V=g["V"].to(dev)))
-        del A, mass, vals, g
-        torch.cuda.empty_cache()
+        nnzb = int(rp_b[T].item())
+        seqs.append(dict(N=n, rp=rp_b[: T + 1].clone(), ci=ci_b[:nnzb].clone(),
+                         vals=vals_b[:nnzb].clone(), nnzb=nnzb, V=g["V"].to(dev)))
+        del A, g
+    del vals_b, ci_b, ws_bm, ws_tp
+    torch.cuda.empty_cache()
     S = len(seqs)
     Ts = [-(-n // B) for n in lens]
     i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)

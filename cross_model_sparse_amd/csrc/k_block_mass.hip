@@ -122,9 +122,13 @@ hipError_t launch_t(const void* A, int H_s, int N, int B, float* mass,
 // triangle); a second kernel adds the heads in a fixed order in fp64.
 // Workgroups go longest row first, consecutive ones on different heads of the
 // same block row.
+// kRagged (N*e not a multiple of VEC, or A off a VEC-byte boundary): rows
+// start off a VEC-byte boundary, so pieces are read with loads aligned only
+// to the element size, and the last block row's final N mod EPV columns are
+// summed one element at a time per row and added to their column block.
 constexpr int kRowThreads = 512;
 
-template <class TT, int VEC, int UNR>
+template <class TT, int VEC, int UNR, bool kRagged>
 __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
     const typename TT::S* __restrict__ A, int H_s, int N, int B, float* __restrict__ part) {
   using S = typename TT::S;
@@ -132,17 +136,31 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
   constexpr int EPV = VEC / (int)sizeof(S);      // elements per piece
   constexpr int NPT = 2;                         // pieces per thread in a wide chunk
   __shared__ double red[NPT * kRowThreads];
+  __shared__ double tail[kRagged ? 128 : 1];     // per-row sum of the ragged columns
+  auto ld = [](const S* q) -> V {
+    if constexpr (kRagged) return load_any<VEC>(q);
+    else return *reinterpret_cast<const V*>(q);
+  };
   const int T = (N + B - 1) / B;
   const int h = blockIdx.x % H_s;
   const int I = T - 1 - (int)(blockIdx.x / H_s);
   const int tid = threadIdx.x;
   const int rows = min(B, N - I * B);
   const int cols = min(N, (I + 1) * B);          // causal columns of these rows
-  const int P = cols / EPV;                      // pieces per row (cols is a multiple of EPV)
+  const int P = cols / EPV;                      // whole pieces per row (>= 1: N >= EPV)
   const int CPJ = B / EPV;                       // pieces per column block
   const int64_t tri = (int64_t)T * (T + 1) / 2;
   float* out = part + (int64_t)h * tri + (int64_t)I * (I + 1) / 2;
   const S* rowbase = A + ((int64_t)h * N + (int64_t)I * B) * N;
+  // ragged columns [P EPV, cols) (last block row only): column block Jt
+  const int tailn = kRagged ? cols - P * EPV : 0;
+  const int Jt = (P * EPV) / B;
+  if (kRagged && tailn > 0 && tid < rows) {
+    const S* q = rowbase + (int64_t)tid * N + (int64_t)P * EPV;
+    float t = 0.f;
+    for (int e = 0; e < tailn; ++e) t += TT::tof(q[e]);
+    tail[tid] = (double)t;
+  }
   for (int c0 = 0; c0 < P; c0 += NPT * kRowThreads) {
     const int CW = min(P - c0, NPT * kRowThreads);  // pieces in this chunk
     // narrow chunk (CW <= kRowThreads): one piece per thread, RPP rows per
@@ -160,12 +178,12 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
         for (; r + (UNR - 1) * RPP < rows; r += UNR * RPP) {
           V v[UNR];
 #pragma unroll
-          for (int u = 0; u < UNR; ++u) v[u] = *reinterpret_cast<const V*>(p + u * step);
+          for (int u = 0; u < UNR; ++u) v[u] = ld(p + u * step);
 #pragma unroll
           for (int u = 0; u < UNR; ++u) acc0 += (double)vec_sum<TT, VEC>(v[u]);
           p += UNR * step;
         }
-        for (; r < rows; r += RPP, p += step) acc0 += (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p));
+        for (; r < rows; r += RPP, p += step) acc0 += (double)vec_sum<TT, VEC>(ld(p));
       }
     } else {
       const bool has1 = c + kRowThreads < CW;
@@ -178,8 +196,8 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
         V v0[U2], v1[U2];
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
-          v0[u] = *reinterpret_cast<const V*>(p0 + (int64_t)(r + u) * N);
-          v1[u] = *reinterpret_cast<const V*>(p1 + (int64_t)(r + u) * N);
+          v0[u] = ld(p0 + (int64_t)(r + u) * N);
+          v1[u] = ld(p1 + (int64_t)(r + u) * N);
         }
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
@@ -189,8 +207,8 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
         }
       }
       for (; r < rows; ++r) {
-        acc0 += (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p0 + (int64_t)r * N));
-        const double s1 = (double)vec_sum<TT, VEC>(*reinterpret_cast<const V*>(p1 + (int64_t)r * N));
+        acc0 += (double)vec_sum<TT, VEC>(ld(p0 + (int64_t)r * N));
+        const double s1 = (double)vec_sum<TT, VEC>(ld(p1 + (int64_t)r * N));
         acc1 += has1 ? s1 : 0.0;
       }
     }
@@ -201,7 +219,11 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
     // held by threads (x % W) + W q, q < RPP, in slot k = x / W.  Chunks start
     // at multiples of NPT * kRowThreads, which CPJ (a power of two <= 128)
     // divides, so no column block spans two chunks.
-    const int j0 = c0 / CPJ, j1 = (c0 + CW - 1) / CPJ;
+    // The ragged columns join the last chunk: their block Jt is the chunk's
+    // last one, or the next one when they start a block of their own (xb = xe).
+    const int j0 = c0 / CPJ;
+    int j1 = (c0 + CW - 1) / CPJ;
+    if (kRagged && tailn > 0 && c0 + CW == P) j1 = max(j1, Jt);
     for (int jj = tid; jj <= j1 - j0; jj += kRowThreads) {
       const int J = j0 + jj;
       const int xb = J * CPJ - c0, xe = min((J + 1) * CPJ, c0 + CW) - c0;
@@ -210,6 +232,8 @@ __global__ __launch_bounds__(kRowThreads) void k_block_mass_rows(
         const int k = x / W, cc = x - k * W;
         for (int q = 0; q < RPP; ++q) s += red[k * kRowThreads + q * W + cc];
       }
+      if (kRagged && tailn > 0 && J == Jt)
+        for (int r = 0; r < rows; ++r) s += tail[r];
       out[J] = (float)s;
     }
     __syncthreads();
@@ -236,12 +260,12 @@ __global__ __launch_bounds__(256) void k_block_mass_heads(const float* __restric
     mass[(int64_t)I * T + J] = J <= I ? (float)((((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]) / (double)H_s) : 0.f;
 }
 
-template <class TT, int VEC>
+template <class TT, int VEC, bool kRagged = false>
 hipError_t launch_rows_t(const void* A, int H_s, int N, int B, float* mass, float* part,
                          hipStream_t st) {
   const int T = mf::blocks_of(N, B);
   const auto* a = reinterpret_cast<const typename TT::S*>(A);
-  hipLaunchKernelGGL((k_block_mass_rows<TT, VEC, 8>), dim3(H_s * T), dim3(kRowThreads), 0, st,
+  hipLaunchKernelGGL((k_block_mass_rows<TT, VEC, 8, kRagged>), dim3(H_s * T), dim3(kRowThreads), 0, st,
                      a, H_s, N, B, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -263,6 +287,12 @@ hipError_t launch_block_mass_rows(const void* A, int dt, int H_s, int N, int B, 
   float* part = reinterpret_cast<float*>(workspace);
   const int esz = dtype_bytes(dt);
   const int vec = row_vec_bytes(A, N, B, esz);
+  if (vec < 16 && ragged_rows_ok(A, N, esz)) {
+    // rows off a 16-byte boundary: 16-byte pieces all the same, ragged end apart
+    if (dt == MF_F32) return launch_rows_t<mfd::TF32, 16, true>(A, H_s, N, B, mass, part, st);
+    if (dt == MF_F16) return launch_rows_t<mfd::TF16, 16, true>(A, H_s, N, B, mass, part, st);
+    return launch_rows_t<mfd::TBF16, 16, true>(A, H_s, N, B, mass, part, st);
+  }
   if (dt == MF_F32) {
     if (vec >= 16) return launch_rows_t<mfd::TF32, 16>(A, H_s, N, B, mass, part, st);
     if (vec >= 8) return launch_rows_t<mfd::TF32, 8>(A, H_s, N, B, mass, part, st);

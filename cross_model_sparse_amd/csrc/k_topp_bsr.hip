@@ -19,7 +19,8 @@
 //  2. k_scan    one workgroup: exclusive scan of the per-row counts -> row_ptr.
 //  3. k_gather  grid-stride over (kept block, group of 8 heads): writes
 //               col_idx and copies the kept tiles into vals with full-width
-//               coalesced loads/stores, zero-padding rows/columns >= N.  It
+//               coalesced loads/stores (16-byte pieces also where map rows
+//               start off a 16-byte boundary), zero-padding rows/columns >= N.  It
 //               reads nnzb = row_ptr[T] on the device and does nothing when
 //               nnzb exceeds the caller's capacity, so no host round trip is
 //               needed between the launches.
@@ -182,7 +183,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(
 constexpr int kGatherThreads = 256;
 constexpr int kHeadsPerUnit = 8;
 
-template <class TT, int VEC>
+// kRagged: map rows start off a VEC-byte boundary (N*e not a multiple of VEC,
+// or A off one): pieces are read with loads aligned only to the element size,
+// and the piece that straddles column N (last column block only) is put
+// together element by element, zero past N.
+template <class TT, int VEC, bool kRagged>
 __global__ __launch_bounds__(kGatherThreads) void k_gather(
     const typename TT::S* __restrict__ A, int H_s, int N, int B,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ kept,
@@ -230,8 +235,19 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(
           const int c = chk * EPV;
           dst[w] = (((k * H_s + h) * B + i) * B + c);
           if (i < rows_valid && c < cols_valid) {
-            v[w] = *reinterpret_cast<const Vt*>(
-                A + ((int64_t)h * N + (int64_t)I * B + i) * N + (int64_t)J * B + c);
+            const S* src = A + ((int64_t)h * N + (int64_t)I * B + i) * N + (int64_t)J * B + c;
+            if constexpr (kRagged) {
+              if (c + EPV <= cols_valid) {
+                v[w] = load_any<VEC>(src);
+              } else {
+                S e[EPV];
+#pragma unroll
+                for (int t = 0; t < EPV; ++t) e[t] = t < cols_valid - c ? src[t] : S{};
+                __builtin_memcpy(&v[w], e, VEC);
+              }
+            } else {
+              v[w] = *reinterpret_cast<const Vt*>(src);
+            }
           } else {
             v[w] = Vt{};
           }
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(
   }
 }
 
-template <class TT, int VEC>
+template <class TT, int VEC, bool kRagged = false>
 hipError_t launch_gather(const void* A, int H_s, int N, int B,
                          const int32_t* row_ptr, const int32_t* kept,
                          int64_t cap, int32_t* col_idx, void* vals,
@@ -255,7 +271,7 @@ hipError_t launch_gather(const void* A, int H_s, int N, int B,
   const int64_t units = ub * HG;
   if (units <= 0) return hipSuccess;
   const int grid = (int)std::min<int64_t>(units, 8192);
-  hipLaunchKernelGGL((k_gather<TT, VEC>), dim3(grid), dim3(kGatherThreads), 0,
+  hipLaunchKernelGGL((k_gather<TT, VEC, kRagged>), dim3(grid), dim3(kGatherThreads), 0,
                      st, reinterpret_cast<const typename TT::S*>(A), H_s, N, B,
                      row_ptr, kept, cap, col_idx,
                      reinterpret_cast<typename TT::S*>(vals));
@@ -267,6 +283,7 @@ hipError_t launch_gather_t(int vec, const void* A, int H_s, int N, int B,
                            const int32_t* row_ptr, const int32_t* kept,
                            int64_t cap, int32_t* col_idx, void* vals,
                            hipStream_t st) {
+  if (vec < 0) return launch_gather<TT, 16, true>(A, H_s, N, B, row_ptr, kept, cap, col_idx, vals, st);
   if (vec >= 16) return launch_gather<TT, 16>(A, H_s, N, B, row_ptr, kept, cap, col_idx, vals, st);
   if (vec >= 8) return launch_gather<TT, 8>(A, H_s, N, B, row_ptr, kept, cap, col_idx, vals, st);
   if (vec >= 4 || sizeof(typename TT::S) == 4)
@@ -300,6 +317,10 @@ hipError_t launch_topp_bsr(const float* mass, const void* A, int dt, int H_s,
   hipError_t e = launch_select_scan(mass, N, B, p, row_ptr, workspace, st);
   if (e != hipSuccess) return e;
   int vec = row_vec_bytes(A, N, B, dtype_bytes(dt));
+  // rows off a 16-byte boundary into a 16-byte aligned vals: the ragged
+  // variant (vec = -1) keeps 16-byte pieces
+  if (vec < 16 && ragged_rows_ok(A, N, dtype_bytes(dt)) && (reinterpret_cast<uintptr_t>(vals) % 16) == 0)
+    vec = -1;
   while (vec > dtype_bytes(dt) && (reinterpret_cast<uintptr_t>(vals) % vec) != 0) vec >>= 1;
   if (dt == MF_F32)
     return launch_gather_t<mfd::TF32>(vec, A, H_s, N, B, row_ptr, kept, cap_nnzb, col_idx, vals, st);

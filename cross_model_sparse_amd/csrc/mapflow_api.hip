@@ -33,6 +33,10 @@ int row_vec_bytes(const void* base, int N, int B, int esize) {
   return esize;
 }
 
+bool ragged_rows_ok(const void* base, int N, int esize) {
+  return (reinterpret_cast<uintptr_t>(base) % esize) == 0 && (int64_t)N * esize >= 16;
+}
+
 }  // namespace mf
 
 namespace {

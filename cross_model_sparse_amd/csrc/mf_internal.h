@@ -20,6 +20,10 @@ inline int dtype_bytes(int dt) { return dt == MF_F32 ? 4 : 2; }
 // Largest load width in bytes (16, 8, 4 or the element size) such that every
 // row segment of a block tile starts on that alignment.
 int row_vec_bytes(const void* base, int N, int B, int esize);
+// True when map rows that miss row_vec_bytes' 16 bytes can still be read in
+// 16-byte pieces with element-aligned loads: A element-aligned and a row at
+// least 16 bytes long (so every block row has a whole piece).
+bool ragged_rows_ok(const void* base, int N, int esize);
 
 // Kernel launchers (one per translation unit); arguments already validated.
 // Row-streaming block mass: per-(head, block row) workgroups into an fp32
@@ -129,6 +133,18 @@ template <> struct VecT<16> { using T = uint4; };
 template <> struct VecT<8> { using T = uint2; };
 template <> struct VecT<4> { using T = unsigned; };
 template <> struct VecT<2> { using T = unsigned short; };
+
+// VEC bytes from an address aligned only to the element size.  The HSA
+// target runs with unaligned global access enabled, so this is still one
+// vector load (the memory path splits it where it crosses a line); it serves
+// map rows that do not start on a VEC-byte boundary (N*e not a multiple of
+// VEC, as in ragged sequence lengths).
+template <int VEC, class S>
+__device__ __forceinline__ typename VecT<VEC>::T load_any(const S* p) {
+  typename VecT<VEC>::T v;
+  __builtin_memcpy(&v, p, VEC);
+  return v;
+}
 
 // Sum, in fp32, of the elements packed in one vector.
 template <class TT, int VEC>

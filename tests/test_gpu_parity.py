@@ -385,3 +385,34 @@ def test_block_mass_variants_agree(gpu, name, ov):
         rel = np.abs(m[tri] - ref[tri]) / np.maximum(np.abs(ref[tri]), 1e-30)
         assert rel.max() <= 1e-6, rel.max()
         assert np.all(np.triu(m, 1) == 0)
+
+
+@pytest.mark.parametrize("name,ov", [("pair14b8b-bf16", dict(N=640, H_s=8)),
+                                     ("pair8b3b-f16", dict(N=333, H_s=8)),
+                                     ("tiny-f32", dict(N=256))])
+def test_map_off_a_16_byte_boundary(gpu, name, ov):
+    # the same map stored one element into a larger buffer: every row starts off
+    # a 16-byte boundary, so block mass and the tile gather take their
+    # element-aligned 16-byte loads; results against the oracle as everywhere
+    w = synth.workload(name, **ov)
+    L = synth.gen_layer(w, device=gpu)
+    A0 = L["A"]
+    buf = torch.empty(A0.numel() + 1, dtype=A0.dtype, device=gpu)
+    A = buf[1:].view(A0.shape)
+    A.copy_(A0)
+    assert A.data_ptr() % 16 != 0
+    say(f"[offset map] {w.name} N={w.N} B={w.B} H_s={w.H_s} {w.dtype}")
+    W, V = L["W"].to(gpu), L["V"].to(gpu)
+    mass, rp, ci, vals, nnzb, O = gpu_pipeline(A, W, V, w.B, w.p)
+    m_strip = mf.block_mass(A, w.B, workspace=False)
+    torch.cuda.synchronize()
+    g_rp = host(rp).astype(np.int64)
+    check_bsr_structure(g_rp, host(ci)[:nnzb], w.T)
+    g_vals = {k: host(vals[k]) for k in range(nnzb)}
+    ties, _ = check_rows(list(range(w.T)), HostView(A0), host(L["W"]), host(L["V"]), w.B, w.p,
+                         w.dtype, host(mass), g_rp, host(ci), g_vals, host(O))
+    assert ties <= 1
+    ref = oracle.block_mass(HostView(A0), w.B)
+    tri = np.tril_indices(w.T)
+    m = host(m_strip)
+    assert (np.abs(m[tri] - ref[tri]) / np.maximum(np.abs(ref[tri]), 1e-30)).max() <= 1e-6
