@@ -20,6 +20,8 @@
 //    bit-reproducible run to run.
 //  * The same workgroup writes the zeros of its strip above the diagonal, so
 //    mass[T][T] is written completely without a separate fill.
+//  * Rows that start off a 16-byte boundary (ragged N) keep 16-byte chunks,
+//    read with loads aligned only to the element size.
 #include "mf_internal.h"
 
 namespace {
@@ -28,13 +30,21 @@ using namespace mfd;
 
 constexpr int kThreads = 256;
 
-template <class TT, int VEC>
+// kRagged: map rows start off a VEC-byte boundary (N*e not a multiple of VEC,
+// or A off one).  Chunks are read with loads aligned only to the element
+// size; the one chunk that straddles column N (last column block) is summed
+// element by element.
+template <class TT, int VEC, bool kRagged>
 __global__ __launch_bounds__(kThreads) void k_block_mass(
     const typename TT::S* __restrict__ A, int H_s, int N, int B, int JPC,
     float* __restrict__ mass) {
   using S = typename TT::S;
   using V = typename VecT<VEC>::T;
   constexpr int EPV = VEC / (int)sizeof(S);  // elements per vector
+  auto ld = [](const S* q) -> V {
+    if constexpr (kRagged) return load_any<VEC>(q);
+    else return *reinterpret_cast<const V*>(q);
+  };
   const int T = (N + B - 1) / B;
   const int I = blockIdx.x;
   const int J0 = blockIdx.y * JPC;
@@ -56,21 +66,28 @@ __global__ __launch_bounds__(kThreads) void k_block_mass(
   const int rows = min(B, N - I * B);
 
   double acc = 0.0;
-  if (col < col_end) {
+  if (col < col_end && (!kRagged || col + EPV <= col_end)) {
     for (int h = 0; h < H_s; ++h) {
       const S* base = A + ((int64_t)h * N + (int64_t)I * B) * N + col;
       int i = r0;
       for (; i + 7 * RPI < rows; i += 8 * RPI) {
         V v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = *reinterpret_cast<const V*>(base + (int64_t)(i + u * RPI) * N);
+        for (int u = 0; u < 8; ++u) v[u] = ld(base + (int64_t)(i + u * RPI) * N);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += (double)vec_sum<TT, VEC>(v[u]);
       }
-      for (; i < rows; i += RPI) {
-        V v = *reinterpret_cast<const V*>(base + (int64_t)i * N);
-        acc += (double)vec_sum<TT, VEC>(v);
+      for (; i < rows; i += RPI) acc += (double)vec_sum<TT, VEC>(ld(base + (int64_t)i * N));
+    }
+  } else if (kRagged && col < col_end) {
+    // the chunk straddling column N: its col_end - col valid elements
+    const int nv = col_end - col;
+    for (int h = 0; h < H_s; ++h) {
+      const S* base = A + ((int64_t)h * N + (int64_t)I * B) * N + col;
+      for (int i = r0; i < rows; i += RPI) {
+        float t = 0.f;
+        for (int e = 0; e < nv; ++e) t += TT::tof(base[(int64_t)i * N + e]);
+        acc += (double)t;
       }
     }
   }
@@ -92,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void k_block_mass(
   }
 }
 
-template <class TT, int VEC>
+template <class TT, int VEC, bool kRagged = false>
 hipError_t launch_t(const void* A, int H_s, int N, int B, float* mass,
                     hipStream_t st) {
   const int esz = (int)sizeof(typename TT::S);
@@ -100,7 +117,7 @@ hipError_t launch_t(const void* A, int H_s, int N, int B, float* mass,
   const int limit = min(1024, kThreads * VEC);     // strip row bytes
   const int JPC = max(1, limit / (B * esz));
   dim3 grid(T, (T + JPC - 1) / JPC);
-  hipLaunchKernelGGL((k_block_mass<TT, VEC>), grid, dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((k_block_mass<TT, VEC, kRagged>), grid, dim3(kThreads), 0, st,
                      reinterpret_cast<const typename TT::S*>(A), H_s, N, B, JPC,
                      mass);
   return hipGetLastError();
@@ -314,6 +331,11 @@ hipError_t launch_block_mass(const void* A, int dt, int H_s, int N, int B,
                              float* mass, hipStream_t st) {
   const int esz = dtype_bytes(dt);
   const int vec = row_vec_bytes(A, N, B, esz);
+  if (vec < 16 && ragged_rows_ok(A, N, esz)) {
+    if (dt == MF_F32) return launch_t<mfd::TF32, 16, true>(A, H_s, N, B, mass, st);
+    if (dt == MF_F16) return launch_t<mfd::TF16, 16, true>(A, H_s, N, B, mass, st);
+    return launch_t<mfd::TBF16, 16, true>(A, H_s, N, B, mass, st);
+  }
   if (dt == MF_F32) {
     if (vec >= 16) return launch_t<mfd::TF32, 16>(A, H_s, N, B, mass, st);
     if (vec >= 8) return launch_t<mfd::TF32, 8>(A, H_s, N, B, mass, st);
