@@ -55,6 +55,13 @@ def parse():
     return ap.parse_args()
 
 
+def launch_stats(us):
+    """Median, 10th and 90th percentile of per-launch times (microseconds)."""
+    v = np.asarray(us, dtype=np.float64)
+    return {"n": int(v.size), "median": float(np.median(v)),
+            "p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90))}
+
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_retrieve_mfma_pair14b8b_bf16_N8192_traffic.txt")
 KERNEL_SRC = os.path.join(HERE, "cross_model_sparse_amd", "csrc", "k_retrieve.hip")
@@ -231,6 +238,7 @@ def main():
         "kernels_ms_per_layer": {"block_mass": t_mass / n_retr * 1e3,
                                  "topp_select_bsr": t_topp / n_retr * 1e3,
                                  "retrieve_fused": t_retr / n_retr * 1e3},
+        "retrieve_fused_launch_us": launch_stats([c.elapsed_time(d) * 1e3 for a, b, c, d in rec]),
         "roofline_kernels": {
             "block_mass_GBs": causal_bytes * K / t_mass / 1e9,
             "topp_select_bsr_GBs": gather_bytes * K / t_topp / 1e9},
