@@ -266,7 +266,8 @@ def qk_leg(dev, reps):
     first layer (N = 4096, B = 64, H_s = 32, d = 128, fp16, p = 0.95; Q, K from
     the workload's seeded recipe), timed with HIP events next to the dense
     path (block mass + selection/gather over the [H_s][N][N] map built from the
-    same Q and K)."""
+    same Q and K).  Two forms: row_lse then block_mass_qk (two passes over the
+    scores), and lse_block_mass_qk (one pass and a small reduction)."""
     import torch
     import cross_model_sparse_amd as mf
     import synth
@@ -301,6 +302,11 @@ def qk_leg(dev, reps):
     t_sel = timed(lambda: mf.topp_select_bsr_qk(mass, Qd, Kd, scale, lse, B, p, cap_nnzb=nnzb,
                                                 row_ptr=rp, col_idx=ci, vals=vals,
                                                 workspace=wsel, sync=False))
+    # lse and masses in one pass over the scores (mf_lse_block_mass_qk)
+    ws1 = torch.empty(mf.lse_block_mass_qk_workspace_bytes(H_s, N, B), dtype=torch.uint8, device=dev)
+    lse1, mass1 = mf.lse_block_mass_qk(Qd, Kd, scale, B, workspace=ws1)
+    t_one = timed(lambda: mf.lse_block_mass_qk(Qd, Kd, scale, B, lse=lse1, out=mass1, workspace=ws1))
+    rp1, ci1, vals1, nnzb1 = mf.topp_select_bsr_qk(mass1, Qd, Kd, scale, lse1, B, p)
     dmass = mf.block_mass(A, B)
     drp, dci, dvals, dnnzb = mf.topp_select_bsr(dmass, A, B, p)
     t_dmass = timed(lambda: mf.block_mass(A, B, out=dmass))
@@ -316,11 +322,14 @@ def qk_leg(dev, reps):
     return {
         "workload": f"pair8b3b-f16 layer 0: N={N}, B={B}, H_s={H_s}, K heads {K.shape[0]}, d={d}, fp16, p={p}",
         "ms": {"row_lse": t_lse, "block_mass_qk": t_mass, "topp_select_bsr_qk": t_sel, "total": total},
+        "one_pass_ms": {"lse_block_mass_qk": t_one, "topp_select_bsr_qk": t_sel,
+                        "total": t_one + t_sel, "nnzb": nnzb1},
         "dense_path_ms": {"block_mass": t_dmass, "topp_select_bsr": t_dsel,
                           "total": t_dmass + t_dsel},
         "dense_map_bytes_not_formed": H_s * N * N * 2,
         "nnzb": nnzb, "nnzb_dense_path": dnnzb,
         "mfma_tflops": {"row_lse": pass_flops / t_lse / 1e9, "block_mass_qk": pass_flops / t_mass / 1e9,
+                        "lse_block_mass_qk": pass_flops / t_one / 1e9,
                         "topp_select_bsr_qk": gather_flops / t_sel / 1e9},
         "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
         "exp_per_s": {"row_lse": H_s * causal_pairs / t_lse * 1e3,

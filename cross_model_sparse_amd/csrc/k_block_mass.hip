@@ -299,6 +299,11 @@ size_t block_mass_rows_workspace_bytes(int H_s, int N, int B) {
   return (size_t)H_s * (size_t)(T * (T + 1) / 2) * sizeof(float);
 }
 
+hipError_t launch_block_mass_heads(const float* part, int H_s, int T, float* mass, hipStream_t st) {
+  hipLaunchKernelGGL(k_block_mass_heads, dim3((T + 63) / 64, T), dim3(256), 0, st, part, H_s, T, mass);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_mass_rows(const void* A, int dt, int H_s, int N, int B, float* mass,
                                   void* workspace, hipStream_t st) {
   float* part = reinterpret_cast<float*>(workspace);

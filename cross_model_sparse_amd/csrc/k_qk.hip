@@ -22,6 +22,7 @@
 // other case (fp32, d = 64/128 with B = 16).
 #include "mf_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace {
@@ -35,6 +36,18 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRT = 16;                         // rows per partial tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+
+// 2^x with the hardware instruction alone: results below 2^-126 may flush to
+// zero, which is harmless inside a sum of terms that include a 1 (log-sum-exp),
+// in probabilities compared at 1e-5 relative (block mass) and in stored tile
+// values (an absolute error below 2^-126)
+__device__ __forceinline__ float exp2_sum(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x of lane l ^ 32 (the other half of the wavefront), by one register swap
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 __device__ __forceinline__ f16x8 as_f16x8(const u32x4& v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -128,6 +141,73 @@ __global__ __launch_bounds__(256) void k_mass_reduce(const float* __restrict__ p
   if (q == 0 && J < T) {
     const double t = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
     mass[(int64_t)I * T + J] = J <= I ? (float)(t / (double)H_s) : 0.f;
+  }
+}
+
+// Per-head block sums from the (m, e) pairs of k_lse_mfma<.., true>:
+//   sums[h][I(I+1)/2 + J] = sum_{i in I} e 2^(m - lse2_i).
+// Workgroup (head, block row I), heaviest rows first, eight wavefronts;
+// wavefront w takes columns J = w, w + 8, ..., two at a time so that their
+// loads overlap.  Lane t holds the pairs t, t + 64 of the block's B rows
+// (contiguous loads); the lanes' terms are added by a fixed fp32 butterfly
+// (at most 128 terms, each at most B: relative error about 2^-21), so the
+// result is bit-reproducible.  launch_block_mass_heads then adds the heads in
+// fp64 in a fixed order.
+constexpr int kMfpThreads = 512;
+__global__ __launch_bounds__(kMfpThreads) void k_mass_from_partials(const float2* __restrict__ part,
+                                                                    const float* __restrict__ lse,
+                                                                    int H_s, int N, int B,
+                                                                    float* __restrict__ sums) {
+  constexpr int kW = kMfpThreads / 64;
+  const int T = (N + B - 1) / B;
+  const int h = blockIdx.x % H_s;
+  const int I = T - 1 - (int)(blockIdx.x / H_s);
+  const int rows = min(B, N - I * B);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* lh = lse + (int64_t)h * N + (int64_t)I * B;
+  // pair t of a block is row t; lane takes t = lane and t = lane + 64
+  constexpr int NP = 2;
+  float l2[NP];
+  bool ok[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int r = lane + 64 * k;
+    ok[k] = r < rows;
+    l2[k] = ok[k] ? lh[r] * kLog2e : 0.f;
+  }
+  const float2* ph = part + (int64_t)h * B * T * (T + 1) / 2 + (int64_t)B * I * (I + 1) / 2;
+  float* out = sums + (int64_t)h * T * (T + 1) / 2 + (int64_t)I * (I + 1) / 2;
+  auto term = [&](const float2& v, int k) {
+    return (ok[k] && v.x > -INFINITY) ? v.y * exp2_sum(v.x - l2[k]) : 0.f;
+  };
+  auto tree = [](float s) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    return s;
+  };
+  for (int J = wave; J <= I; J += 2 * kW) {
+    const int J2 = J + kW;
+    const bool has2 = J2 <= I;
+    const float2* p1 = ph + (int64_t)J * B;
+    const float2* p2 = ph + (int64_t)(has2 ? J2 : J) * B;
+    float2 a[NP], b[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      a[k] = ok[k] ? p1[lane + 64 * k] : make_float2(-INFINITY, 0.f);
+      b[k] = ok[k] ? p2[lane + 64 * k] : make_float2(-INFINITY, 0.f);
+    }
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      s1 += term(a[k], k);
+      s2 += term(b[k], k);
+    }
+    s1 = tree(s1);
+    s2 = tree(s2);
+    if (lane == 0) {
+      out[J] = s1;
+      if (has2) out[J2] = s2;
+    }
   }
 }
 
@@ -324,12 +404,6 @@ __device__ __forceinline__ void qk_walk(const unsigned short* __restrict__ Q,
   }
 }
 
-// 2^x with the hardware instruction alone: results below 2^-126 may flush to
-// zero, which is harmless inside a sum of terms that include a 1 (log-sum-exp),
-// in probabilities compared at 1e-5 relative (block mass) and in stored tile
-// values (an absolute error below 2^-126)
-__device__ __forceinline__ float exp2_sum(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Work item of a workgroup of the lse / mass kernels: row group grp of head
 // h.  The longest groups (most causal key tiles) of every head come first, so
 // the workgroups that share a CU mix long and short walks; workgroups with
@@ -347,10 +421,20 @@ __device__ __forceinline__ int tile_key(int lane, int e) { return 8 * (e >> 2) +
 // written: sched_barrier keeps the compiler from gathering the MFMAs.
 #define MF_PIN() __builtin_amdgcn_sched_barrier(0)
 
-template <bool kBF16, int D>
+// kMass: the same walk also leaves, for every row i and causal column block J,
+// the pair (m, e) with e = sum over the block's keys j of 2^(x_ij - m) and m
+// the row's running maximum after the block (log2 units), in
+// part[h][B (I(I+1)/2 + J) + i - I B], I = i / B (rows fastest, so a
+// wavefront's 32 rows store one contiguous run).  The block's share of
+// the softmax row is then e 2^(m - lse2_i), and k_mass_from_partials forms
+// the block masses from these pairs and lse without a second pass over the
+// scores.  Both halves of the workgroup split the key tiles at a column-block
+// boundary, so each block's pair comes from one half.
+template <bool kBF16, int D, bool kMass>
 __global__ __launch_bounds__(kQkThreads, 4) void k_lse_mfma(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K, int H_s,
-    int H_ks, int N, const float* __restrict__ scale, float* __restrict__ lse) {
+    int H_ks, int N, const float* __restrict__ scale, float* __restrict__ lse, int B,
+    float2* __restrict__ part) {
   constexpr int NKS = D / 16;
   constexpr int EPS = 16 / NKS;                  // scores per MFMA step
   __shared__ __align__(16) unsigned char smem[4 * KTile<D>::kBytes];
@@ -368,24 +452,59 @@ __global__ __launch_bounds__(kQkThreads, 4) void k_lse_mfma(
   const int q0 = R0 + 32 * (wave % kQkHalfWaves);
   const int row = q0 + (lane & 31);
   float m = -INFINITY, l = 0.f;                  // running maximum and sum, log2 units
-  qk_walk<kBF16, D>(Q, K, h, g, N, R0, 1, neg, smem, [&](int kt, const f32x16& c, auto&& mf) {
+  float lb = 0.f;                                // kMass: this block's sum, relative to m
+  const int tpb = kMass ? B / 32 : 1;            // key tiles per column block
+  // kMass: store the pair of block J.  Lanes l and l+32 hold the same row over
+  // different keys; their pairs are merged through one half-wave register
+  // swap (v_permlane32_swap, no LDS round trip).  This wavefront's rows all
+  // lie in block row I (B >= 32, q0 a multiple of 32); the address is formed
+  // here from a wave-uniform base and a 32-bit lane offset, so no pointer
+  // stays live across the walk.
+  auto emit = [&](int J) {
+    const float m2 = other_half(m), e2 = other_half(lb);
+    const float mm = fmaxf(m, m2);
+    const float e = (m > -INFINITY ? lb * exp2_sum(m - mm) : 0.f) +
+                    (m2 > -INFINITY ? e2 * exp2_sum(m2 - mm) : 0.f);
+    const int I = __builtin_amdgcn_readfirstlane(q0 / B);
+    const int T = (N + B - 1) / B;
+    const int64_t base = (int64_t)h * B * T * (T + 1) / 2 + (int64_t)B * I * (I + 1) / 2;
+    if (lane < 32 && row < N) part[base + (unsigned)(J * B + row - I * B)] = make_float2(mm, e);
+    lb = 0.f;
+  };
+  qk_walk<kBF16, D>(Q, K, h, g, N, R0, tpb, neg, smem, [&](int kt, const f32x16& c, auto&& mf) {
     if (kt * 32 + 31 <= q0 && q0 + 31 < N) {    // every key of the tile is causal for every row
       // sc >= 0: the maximum of sc * c is sc times the maximum of c
       float r = c[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) r = fmaxf(r, c[e]);
       const float mx = fmaxf(m, r * sc);
-      float s = l * exp2_sum(m - mx);
+      if constexpr (kMass) {
+        const float f = exp2_sum(m - mx);
+        float t = 0.f;
 #pragma unroll
-      for (int k = 0; k < NKS; ++k) {
-        MF_PIN();
-        mf(k);
-        MF_PIN();
+        for (int k = 0; k < NKS; ++k) {
+          MF_PIN();
+          mf(k);
+          MF_PIN();
 #pragma unroll
-        for (int e = k * EPS; e < (k + 1) * EPS; ++e) s += exp2_sum(fmaf(c[e], sc, -mx));
+          for (int e = k * EPS; e < (k + 1) * EPS; ++e) t += exp2_sum(fmaf(c[e], sc, -mx));
+        }
+        MF_PIN();
+        l = fmaf(l, f, t);
+        lb = fmaf(lb, f, t);
+      } else {
+        float s = l * exp2_sum(m - mx);
+#pragma unroll
+        for (int k = 0; k < NKS; ++k) {
+          MF_PIN();
+          mf(k);
+          MF_PIN();
+#pragma unroll
+          for (int e = k * EPS; e < (k + 1) * EPS; ++e) s += exp2_sum(fmaf(c[e], sc, -mx));
+        }
+        MF_PIN();
+        l = s;
       }
-      MF_PIN();
-      l = s;
       m = mx;
     } else {
 #pragma unroll
@@ -399,12 +518,25 @@ __global__ __launch_bounds__(kQkThreads, 4) void k_lse_mfma(
         mx = fmaxf(mx, x[e]);
       }
       if (mx > -INFINITY) {
-        float s = l * exp2_sum(m - mx);
+        if constexpr (kMass) {
+          const float f = exp2_sum(m - mx);
+          float t = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s += exp2_sum(x[e] - mx);
-        l = s;
+          for (int e = 0; e < 16; ++e) t += exp2_sum(x[e] - mx);
+          l = fmaf(l, f, t);
+          lb = fmaf(lb, f, t);
+        } else {
+          float s = l * exp2_sum(m - mx);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s += exp2_sum(x[e] - mx);
+          l = s;
+        }
         m = mx;
       }
+    }
+    if constexpr (kMass) {
+      // the block's last tile, or the last tile these rows reach
+      if (kt % tpb == tpb - 1 || (kt + 1) * 32 > q0 + 31 || (kt + 1) * 32 >= N) emit(kt / tpb);
     }
   });
   // merge (max, sum) pairs: lanes l and l+32 of a wavefront hold the same row,
@@ -743,14 +875,23 @@ hipError_t gather_plain(const void* Q, const void* K, int H_s, int H_ks, int N, 
   return hipGetLastError();
 }
 
+// part == nullptr: lse only; otherwise also the (m, e) pairs of block size B
 template <bool kBF16>
 hipError_t lse_mfma(const void* Q, const void* K, int H_s, int H_ks, int N, int d,
-                    const float* scale, float* lse, hipStream_t st) {
+                    const float* scale, float* lse, hipStream_t st, int B = 32,
+                    float2* part = nullptr) {
   auto q = reinterpret_cast<const unsigned short*>(Q);
   auto k = reinterpret_cast<const unsigned short*>(K);
   const dim3 grid(H_s * ((N + kQkRows - 1) / kQkRows));
-  if (d == 128) hipLaunchKernelGGL((k_lse_mfma<kBF16, 128>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, scale, lse);
-  else hipLaunchKernelGGL((k_lse_mfma<kBF16, 64>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, scale, lse);
+#define MF_LSE(D_, M_) \
+  hipLaunchKernelGGL((k_lse_mfma<kBF16, D_, M_>), grid, dim3(kQkThreads), 0, st, q, k, H_s, H_ks, N, \
+                     scale, lse, B, part)
+  if (part) {
+    if (d == 128) MF_LSE(128, true); else MF_LSE(64, true);
+  } else {
+    if (d == 128) MF_LSE(128, false); else MF_LSE(64, false);
+  }
+#undef MF_LSE
   return hipGetLastError();
 }
 
@@ -836,6 +977,40 @@ hipError_t launch_block_mass_qk(const void* Q, const void* K, const float* scale
   hipLaunchKernelGGL(k_mass_reduce, dim3(blocks_of(N, B), (blocks_of(N, B) + 63) / 64), dim3(256), 0,
                      st, part, H_s, N, B, mass);
   return hipGetLastError();
+}
+
+// workspace of the one-pass form: the (m, e) pairs, then the per-head block sums
+static size_t lse_pairs_bytes(int H_s, int N, int B) {
+  const size_t T = (size_t)blocks_of(N, B);
+  return ((size_t)H_s * (size_t)B * (T * (T + 1) / 2) * sizeof(float2) + 255) & ~(size_t)255;
+}
+
+size_t lse_block_mass_qk_workspace_bytes(int H_s, int N, int B) {
+  const size_t T = (size_t)blocks_of(N, B);
+  const size_t one = lse_pairs_bytes(H_s, N, B) + (size_t)H_s * (T * (T + 1) / 2) * sizeof(float);
+  return std::max(one, block_mass_qk_workspace_bytes(H_s, N, B));
+}
+
+hipError_t launch_lse_block_mass_qk(const void* Q, const void* K, const float* scale, int dt,
+                                    int H_s, int H_ks, int N, int d, int B, float* lse,
+                                    float* mass, void* workspace, hipStream_t st) {
+  if (!(qk_mfma(dt, d, Q, K) && B >= 32)) {      // two passes: lse, then the masses
+    const hipError_t e = launch_row_lse(Q, K, dt, H_s, H_ks, N, d, scale, lse, st);
+    if (e != hipSuccess) return e;
+    return launch_block_mass_qk(Q, K, scale, lse, dt, H_s, H_ks, N, d, B, mass, workspace, st);
+  }
+  float2* part = reinterpret_cast<float2*>(workspace);
+  float* sums = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) +
+                                         lse_pairs_bytes(H_s, N, B));
+  const int T = blocks_of(N, B);
+  hipError_t e = dt == MF_BF16 ? lse_mfma<true>(Q, K, H_s, H_ks, N, d, scale, lse, st, B, part)
+                               : lse_mfma<false>(Q, K, H_s, H_ks, N, d, scale, lse, st, B, part);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_mass_from_partials, dim3(H_s * T), dim3(kMfpThreads), 0, st, part, lse, H_s, N, B,
+                     sums);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_block_mass_heads(sums, H_s, T, mass, st);
 }
 
 hipError_t launch_gather_qk(const void* Q, const void* K, const float* scale, const float* lse,

@@ -184,6 +184,28 @@ size_t mf_block_mass_qk_workspace_bytes(int H_s, int N, int B) {
   return mf::block_mass_qk_workspace_bytes(H_s, N, B);
 }
 
+size_t mf_lse_block_mass_qk_workspace_bytes(int H_s, int N, int B) {
+  if (H_s < 1 || H_s > 64 || N < 1 || !valid_block(B)) return 0;
+  return mf::lse_block_mass_qk_workspace_bytes(H_s, N, B);
+}
+
+int mf_lse_block_mass_qk(const void* Q, const void* K, const float* scale, int dtype, int H_s,
+                         int H_ks, int N, int d, int B, float* lse, float* mass,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mf_lse_block_mass_qk";
+  int st = check_qk(fn, dtype, H_s, H_ks, N, d, B);
+  if (st != MF_OK) return st;
+  if (!Q || !K || !scale || !lse || !mass || !workspace)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  const size_t need = mf::lse_block_mass_qk_workspace_bytes(H_s, N, B);
+  if (workspace_bytes < need)
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + fmt(": workspace of %lld bytes < %lld required",
+                                                          (long long)workspace_bytes, (long long)need));
+  return mf::hip_check(mf::launch_lse_block_mass_qk(Q, K, scale, dtype, H_s, H_ks, N, d, B, lse, mass,
+                                                    workspace, (hipStream_t)stream),
+                       "mf_lse_block_mass_qk launch");
+}
+
 int mf_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
                      int dtype, int H_s, int H_ks, int N, int d, int B, float* mass,
                      void* workspace, size_t workspace_bytes, void* stream) {

@@ -29,6 +29,9 @@ bool ragged_rows_ok(const void* base, int N, int esize);
 // Row-streaming block mass: per-(head, block row) workgroups into an fp32
 // workspace of block_mass_rows_workspace_bytes, then a fixed-order head sum.
 size_t block_mass_rows_workspace_bytes(int H_s, int N, int B);
+// mass[I][J] = (1/H_s) sum_h part[h][I(I+1)/2 + J] in fp64, head order fixed;
+// zeros above the diagonal (part: H_s * T(T+1)/2 fp32 per-head block sums)
+hipError_t launch_block_mass_heads(const float* part, int H_s, int T, float* mass, hipStream_t st);
 hipError_t launch_block_mass_rows(const void* A, int dt, int H_s, int N, int B, float* mass,
                                   void* workspace, hipStream_t st);
 hipError_t launch_block_mass(const void* A, int dt, int H_s, int N, int B,
@@ -44,6 +47,12 @@ hipError_t launch_select_scan(const float* mass, int N, int B, float p, int32_t*
 hipError_t launch_row_lse(const void* Q, const void* K, int dt, int H_s, int H_ks, int N, int d,
                           const float* scale, float* lse, hipStream_t st);
 size_t block_mass_qk_workspace_bytes(int H_s, int N, int B);
+// lse and block masses in one pass over the scores ((m, e) pairs per row and
+// column block in the workspace, then a fixed-order reduction)
+size_t lse_block_mass_qk_workspace_bytes(int H_s, int N, int B);
+hipError_t launch_lse_block_mass_qk(const void* Q, const void* K, const float* scale, int dt,
+                                    int H_s, int H_ks, int N, int d, int B, float* lse,
+                                    float* mass, void* workspace, hipStream_t st);
 hipError_t launch_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
                                 int dt, int H_s, int H_ks, int N, int d, int B, float* mass,
                                 void* workspace, hipStream_t st);

@@ -25,7 +25,8 @@ _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
             "mf_block_mass_ws_bytes", "mf_block_mass_ws",
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
-            "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk", "mf_topp_select_bsr_qk",
+            "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk",
+            "mf_lse_block_mass_qk_workspace_bytes", "mf_lse_block_mass_qk", "mf_topp_select_bsr_qk",
             "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
             "mf_retrieve_fused_multi", "mf_retrieve_fused_varlen", "mf_prefix_hashes",
             "mf_bm_create", "mf_bm_destroy", "mf_bm_lookup", "mf_bm_release", "mf_bm_insert",
@@ -84,6 +85,11 @@ def load() -> ctypes.CDLL:
     L.mf_block_mass_qk.restype = c_int
     L.mf_block_mass_qk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int,
                                    c_int, c_vp, c_vp, c_sz, c_vp]
+    L.mf_lse_block_mass_qk_workspace_bytes.restype = c_sz
+    L.mf_lse_block_mass_qk_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    L.mf_lse_block_mass_qk.restype = c_int
+    L.mf_lse_block_mass_qk.argtypes = [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_vp, c_vp, c_vp, c_sz, c_vp]
     L.mf_topp_select_bsr_qk.restype = c_int
     L.mf_topp_select_bsr_qk.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                         c_int, c_int, c_f, c_vp, c_vp, c_vp, c_i64,
@@ -409,6 +415,30 @@ def block_mass_qk(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor, lse: to
     return out
 
 
+def lse_block_mass_qk_workspace_bytes(H_s: int, N: int, B: int) -> int:
+    return int(load().mf_lse_block_mass_qk_workspace_bytes(H_s, N, B))
+
+
+def lse_block_mass_qk(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor, B: int,
+                      lse: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """(lse[H_s][N], mass[T][T]) fp32 in one pass over the scores
+    (mf_lse_block_mass_qk)."""
+    H_s, H_ks, N, d = _qk_shapes(Q, K, scale)
+    T = -(-N // B)
+    if lse is None:
+        lse = torch.empty(H_s, N, dtype=torch.float32, device=Q.device)
+    if out is None:
+        out = torch.empty(T, T, dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, lse_block_mass_qk_workspace_bytes(H_s, N, B)),
+                                dtype=torch.uint8, device=Q.device)
+    _check(load().mf_lse_block_mass_qk(_ptr(Q), _ptr(K), _ptr(scale), _dcode(Q), H_s, H_ks, N, d,
+                                       B, _ptr(lse), _ptr(out), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
+    return lse, out
+
+
 def topp_select_bsr_qk(mass: torch.Tensor, Q: torch.Tensor, K: torch.Tensor,
                        scale: torch.Tensor, lse: torch.Tensor, B: int, p: float,
                        cap_nnzb: int | None = None, row_ptr=None, col_idx=None, vals=None,
@@ -449,11 +479,13 @@ def topp_select_bsr_qk(mass: torch.Tensor, Q: torch.Tensor, K: torch.Tensor,
 
 def compress_qk(Q: torch.Tensor, K: torch.Tensor, scale: torch.Tensor, B: int, p: float,
                 lse: torch.Tensor | None = None, cap_nnzb: int | None = None, stream=None):
-    """Compression without a dense map: (lse, mass, row_ptr, col_idx, vals, nnzb);
-    lse is computed with row_lse when not given."""
+    """Compression without a dense map: (lse, mass, row_ptr, col_idx, vals, nnzb).
+    Without a given lse, lse and the masses come from one pass over the scores
+    (lse_block_mass_qk); with one, the masses from block_mass_qk."""
     if lse is None:
-        lse = row_lse(Q, K, scale, stream=stream)
-    mass = block_mass_qk(Q, K, scale, lse, B, stream=stream)
+        lse, mass = lse_block_mass_qk(Q, K, scale, B, stream=stream)
+    else:
+        mass = block_mass_qk(Q, K, scale, lse, B, stream=stream)
     row_ptr, col_idx, vals, nnzb = topp_select_bsr_qk(mass, Q, K, scale, lse, B, p,
                                                       cap_nnzb=cap_nnzb, stream=stream)
     return lse, mass, row_ptr, col_idx, vals, nnzb

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 4
+#define MF_ABI_VERSION 5
 
 typedef enum {
   MF_OK = 0,
@@ -187,6 +187,31 @@ size_t mf_block_mass_qk_workspace_bytes(int H_s, int N, int B);
 int mf_block_mass_qk(const void* Q, const void* K, const float* scale, const float* lse,
                      int dtype, int H_s, int H_ks, int N, int d, int B, float* mass,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mf_lse_block_mass_qk needs: H_s * B * T(T+1)/2 pairs of
+ * float32 (one per row and causal column block) and H_s * T(T+1)/2 float32
+ * per-head block sums, or the workspace of mf_block_mass_qk where that is
+ * larger. */
+size_t mf_lse_block_mass_qk_workspace_bytes(int H_s, int N, int B);
+
+/*
+ * mf_row_lse and mf_block_mass_qk in one pass over the scores: lse (device,
+ * [H_s][N] float32) and mass (device, [T][T] float32, written completely) as
+ * those two calls define them.  While the online maximum and sum of a row run
+ * over its keys, the pass also keeps, for each causal column block J, the
+ * block's sum e = sum_{j in J} exp(s - m) relative to the row's running
+ * maximum m after the block; then
+ *   mass[I][J] = (1/H_s) * sum_h sum_{i in I} e_h[i][J] * exp(m_h[i][J] - lse[h][i]):
+ * each head's terms over a block row are added in fp32 in a fixed tree order,
+ * the heads in fp64 in a fixed order (bit-reproducible).  Each (m, e) pair is
+ * an fp32 pair; the result agrees with mf_block_mass_qk's direct sums to
+ * fp32 rounding.  The scores are computed once instead of twice.  fp32 inputs
+ * and B = 16 take the two separate passes.  workspace: device, >=
+ * mf_lse_block_mass_qk_workspace_bytes.  Errors as mf_block_mass_qk.
+ */
+int mf_lse_block_mass_qk(const void* Q, const void* K, const float* scale, int dtype, int H_s,
+                         int H_ks, int N, int d, int B, float* lse, float* mass,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Block-level Top-p selection and BSR build as mf_topp_select_bsr (same rule,

@@ -177,3 +177,55 @@ def test_qk_repeat_runs_are_bitwise_identical():
     for x, y in zip(a[:5], b[:5]):
         assert torch.equal(x, y)
     assert a[5] == b[5]
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_lse_and_mass_in_one_pass(name, cfg):
+    # mf_lse_block_mass_qk: lse against the oracle; masses against the oracle
+    # on the map the library's lse defines (the oracle takes the same fp32
+    # values) and against the two-pass mf_block_mass_qk; repeat runs identical
+    H_s, H_ks, N, d, B, dt, p = cfg[:7]
+    smul = cfg[7] if len(cfg) > 7 else 1.0
+    say(f"[qk one pass] {name} H_s={H_s} H_ks={H_ks} N={N} d={d} B={B} {dt} scale x {smul}")
+    Q, K, scale = make_inputs(zlib.crc32(name.encode()) % 10000, H_s, H_ks, N, d, dt)
+    scale = scale * smul
+    Qh, Kh, sch = host(Q), host(K), scale.double().numpy()
+    dev = torch.device("cuda:0")
+    Qd, Kd, scd = Q.to(dev), K.to(dev), scale.to(dev)
+    T = -(-N // B)
+    lse_g, mass_g = mf.lse_block_mass_qk(Qd, Kd, scd, B)
+    lse_g2, mass_g2 = mf.lse_block_mass_qk(Qd, Kd, scd, B)
+    mass_two = mf.block_mass_qk(Qd, Kd, scd, lse_g, B)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_g, lse_g2) and torch.equal(mass_g, mass_g2)
+    lse_h = host(lse_g)
+    assert np.abs(lse_h - oracle.row_lse(Qh, Kh, sch)).max() <= N * 2.0 ** -24 + 1e-5
+    m1, m2 = host(mass_g), host(mass_two)
+    assert np.all(np.triu(m1, 1) == 0)
+    mass_ref = oracle.block_mass(oracle.QKMap(Qh, Kh, sch, lse_h.astype(np.float64)), B)
+    tri = np.tril_indices(T)
+    tol = 16 * B * 2.0 ** -24 + 1e-5
+    for m in (m1, m2):
+        rel = np.abs(m[tri] - mass_ref[tri]) / np.maximum(np.abs(mass_ref[tri]), 1e-30)
+        assert rel.max() <= tol, f"mass max rel err {rel.max():.3e}"
+
+
+def test_lse_and_mass_in_one_pass_full_size():
+    # the 8B->3B-like shape, sampled block rows against the oracle
+    H_s, H_ks, N, d, B, dt = 32, 8, 4096, 128, 64, "f16"
+    say(f"[qk one pass] full size H_s={H_s} N={N}")
+    Q, K, scale = make_inputs(4242, H_s, H_ks, N, d, dt)
+    Qh, Kh, sch = host(Q), host(K), scale.double().numpy()
+    dev = torch.device("cuda:0")
+    Qd, Kd, scd = Q.to(dev), K.to(dev), scale.to(dev)
+    lse_g, mass_g = mf.lse_block_mass_qk(Qd, Kd, scd, B)
+    mass_h, lse_h = host(mass_g), host(lse_g)
+    T = N // B
+    for I in (0, 1, T // 2, T - 1):
+        rows = np.arange(I * B, (I + 1) * B)
+        assert np.abs(lse_h[:, rows] - oracle.row_lse(Qh, Kh, sch, rows=rows)).max() <= N * 2.0 ** -24 + 1e-5
+        lse_view = np.zeros((H_s, N))
+        lse_view[:, rows] = lse_h[:, rows]
+        m_ref = oracle.block_mass_row(oracle.QKMap(Qh, Kh, sch, lse_view), B, I)
+        rel = np.abs(mass_h[I, : I + 1] - m_ref) / np.maximum(m_ref, 1e-30)
+        assert rel.max() <= 16 * B * 2.0 ** -24 + 1e-5, (I, rel.max())
