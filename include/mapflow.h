@@ -81,6 +81,11 @@ const char* mf_last_error(void);
  *  mass  device, [T][T] float32, written completely.
  *  The per-block sum is formed with fp32 partial sums of at most 8
  *  consecutive elements combined in fp64, then rounded once to fp32.
+ *  Alignment: A needs only its element alignment.  Rows of N*e bytes that
+ *  are not a multiple of 16 (ragged N, or A off a 16-byte boundary) are read
+ *  with 16-byte loads aligned to the element size, which the HSA target's
+ *  unaligned global access allows; rows shorter than 16 bytes use narrower
+ *  loads.
  *  Errors: MF_ERR_INVALID for a null pointer, N < 1, B not in
  *  {16,32,64,128}, H_s not in [1,64] or an unknown dtype.
  */
