@@ -338,3 +338,39 @@ def test_block_mass_ws_size_and_rejects(L):
     assert L.mf_block_mass_ws(*args, FAKE, need - 1, None) == mf.MF_ERR_INVALID
     assert "workspace" in _last(L)
     assert L.mf_block_mass_ws(FAKE, 2, 40, 8192, 48, FAKE, FAKE, need, None) == mf.MF_ERR_INVALID
+
+
+# ---- the header as plain C ----------------------------------------------------
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "mapflow.h"
+int main(void) {
+  if (mf_abi_version() != MF_ABI_VERSION) return 1;
+  if (strncmp(mf_status_string(MF_ERR_INVALID), "MF_ERR_INVALID", 14) != 0) return 2;
+  /* an argument error is reported, not thrown: N = 0 */
+  if (mf_block_mass((const void*)16, MF_BF16, 4, 0, 64, (float*)16, NULL) != MF_ERR_INVALID) return 3;
+  if (strlen(mf_last_error()) == 0) return 4;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_is_c_and_a_c_program_links_and_runs(tmp_path):
+    # the boundary is a C ABI: the header compiles as pedantic C99, and a C
+    # caller links against the library and gets statuses back (no GPU call)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc = os.path.join(root, "include")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                    "-x", "c", os.path.join(inc, "mapflow.h")], check=True)
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    libdir = os.path.dirname(mf.lib_path())
+    exe = tmp_path / "caller"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", inc, str(src), "-L", libdir,
+                    "-lmapflow", "-o", str(exe)], check=True)
+    env = dict(os.environ, LD_LIBRARY_PATH=libdir + os.pathsep + os.environ.get("LD_LIBRARY_PATH", ""))
+    out = subprocess.run([str(exe)], env=env, capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr)
