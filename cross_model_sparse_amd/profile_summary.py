@@ -12,8 +12,9 @@
         FETCH_SIZE, one with WRITE_SIZE, both KiB per dispatch).  Each counter is
         scaled by what it reads for a plain copy kernel of known size run in the
         same command (M MiB read and M MiB written per launch, run by
-        bench.py --copy-ref-mib M).  The record carries the SHA-256 of the retrieval kernel source so
-        a reader can tell whether the kernel changed since.
+        bench.py --copy-ref-mib M).  The record carries the SHA-256 of the kernel's
+        source (--source, default the retrieval kernel's) so a reader can tell
+        whether the kernel changed since.
 """
 from __future__ import annotations
 
@@ -54,17 +55,25 @@ def _dispatches(path: str, counter: str):
     return rows
 
 
-def _copy_reference(rows, kernel: str, mib: int):
-    """Counter values of the copy reference.  bench.py --copy-ref-mib runs it
-    after the capacity pass and before the first timed step, so it is the set
-    of elementwise dispatches between the last gather before the step's first
-    block-mass launch and that launch (the fill that creates the source reads
+def _reference_window(rows):
+    """(lo, hi): bench.py --copy-ref-mib runs the copy reference after the
+    capacity pass and before the first timed step, so it lies strictly between
+    the capacity pass's last gather (lo) and the step's first block-mass
+    launches (hi: the last block-mass dispatch before the step's first
+    retrieval launch)."""
+    first = next(i for i, r in enumerate(rows) if "k_retrieve_mfma" in r[1])
+    hi = max(i for i in range(first) if "k_block_mass" in rows[i][1])
+    lo = max(i for i in range(hi) if "k_gather" in rows[i][1])
+    return lo, hi
+
+
+def _copy_reference(rows, mib: int):
+    """Counter value of the copy reference: the median of the elementwise
+    dispatches in the reference window (the fill that creates the source reads
     nothing and is skipped by the > 1/4 size test in the fetch run)."""
     want = mib * 1024.0
-    first = next(i for i, r in enumerate(rows) if kernel in r[1])
-    step_bm = max(i for i in range(first) if "k_block_mass" in rows[i][1])
-    last_gather = max(i for i in range(step_bm) if "k_gather" in rows[i][1])
-    vals = [v for _, name, v in rows[last_gather + 1:step_bm]
+    lo, hi = _reference_window(rows)
+    vals = [v for _, name, v in rows[lo + 1:hi]
             if "elementwise" in name and v > 0.25 * want]
     if not vals:
         raise SystemExit("no copy-reference dispatch found in the counter file")
@@ -72,29 +81,38 @@ def _copy_reference(rows, kernel: str, mib: int):
     return vals[len(vals) // 2]
 
 
-def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd) -> str:
+def _kernel_mean(rows, kernel: str):
+    """Mean counter value (KiB) and count of `kernel`'s dispatches after the
+    capacity pass (the timed steps' launches)."""
+    lo, _ = _reference_window(rows)
+    vals = [v for _, name, v in rows[lo + 1:] if kernel in name]
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel} after the capacity pass")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERNEL_SRC) -> str:
     fetch = _dispatches(fetch_csv, "FETCH_SIZE")
     write = _dispatches(write_csv, "WRITE_SIZE")
     want = mib * 1024.0
-    f_ref = _copy_reference(fetch, kernel, mib)
-    w_ref = _copy_reference(write, kernel, mib)
+    f_ref = _copy_reference(fetch, mib)
+    w_ref = _copy_reference(write, mib)
     f_scale = want / f_ref
     w_scale = want / w_ref
-    kf = [v for _, name, v in fetch if kernel in name]
-    kw = [v for _, name, v in write if kernel in name]
-    f_kib = sum(kf) / len(kf)
-    w_kib = sum(kw) / len(kw)
+    f_kib, nf = _kernel_mean(fetch, kernel)
+    w_kib, nw = _kernel_mean(write, kernel)
     fb = f_kib * 1024 * f_scale
     wb = w_kib * 1024 * w_scale
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    src_hash = hashlib.sha256(open(source, "rb").read()).hexdigest()
     lines = [
         f"# HBM traffic of {kernel} from hardware counters",
         f"# fetch run: {fetch_cmd}",
         f"# write run: {write_cmd}",
         f"kernel: {kernel}",
+        f"kernel_source: {os.path.relpath(source, os.path.dirname(HERE))}",
         f"kernel_source_sha256: {src_hash}",
-        f"dispatches_fetch_run: {len(kf)}",
-        f"dispatches_write_run: {len(kw)}",
+        f"dispatches_fetch_run: {nf}",
+        f"dispatches_write_run: {nw}",
         f"FETCH_SIZE_KiB_per_dispatch: {f_kib:.1f}",
         f"WRITE_SIZE_KiB_per_dispatch: {w_kib:.1f}",
         f"copy_reference_MiB_read_and_written: {mib}",
@@ -125,12 +143,15 @@ def main(argv=None):
     t.add_argument("--kernel", default="k_retrieve_mfma")
     t.add_argument("--fetch-command", required=True)
     t.add_argument("--write-command", required=True)
+    t.add_argument("--source", default=KERNEL_SRC,
+                   help="kernel source file whose SHA-256 the record carries "
+                        "(default: the retrieval kernel's)")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats(a.csv, a.command, a.top, a.match))
     else:
         sys.stdout.write(traffic(a.fetch, a.write, a.copy_mib, a.kernel, a.fetch_command,
-                                 a.write_command))
+                                 a.write_command, a.source))
 
 
 if __name__ == "__main__":

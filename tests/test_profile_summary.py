@@ -92,3 +92,17 @@ def test_committed_traffic_record_is_well_formed():
                                          "hbm_bytes_per_launch"))
     assert hb == pytest.approx(fb + wb, abs=2)
     assert len(kv["kernel_source_sha256"]) == 64
+
+
+def test_traffic_of_a_kernel_that_also_runs_in_the_capacity_pass(tmp_path):
+    # block mass runs before the copy reference too; only the step's dispatches count
+    f_rows, w_rows = _run(fetch_ref=131072.0, write_ref=262144.0, k_fetch=1.0, k_write=1.0)
+    f_rows[0] = ("k_block_mass<x>", 999.0)       # capacity pass: excluded
+    _write(tmp_path / "f.csv", "FETCH_SIZE", f_rows)
+    _write(tmp_path / "w.csv", "WRITE_SIZE", w_rows)
+    rec = ps.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 256, "k_block_mass", "a", "b",
+                     source=ps.__file__)
+    kv = dict(line.split(": ", 1) for line in rec.splitlines() if not line.startswith("#"))
+    assert float(kv["FETCH_SIZE_KiB_per_dispatch"]) == pytest.approx(5.0)
+    assert kv["dispatches_fetch_run"] == "2"
+    assert kv["kernel_source"].endswith("profile_summary.py")
