@@ -106,6 +106,7 @@ def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERN
     src_hash = hashlib.sha256(open(source, "rb").read()).hexdigest()
     lines = [
         f"# HBM traffic of {kernel} from hardware counters",
+        "# REPO = repository root",
         f"# fetch run: {fetch_cmd}",
         f"# write run: {write_cmd}",
         f"kernel: {kernel}",
