@@ -256,9 +256,35 @@ def main():
         out["prefix_cache"] = cache_leg(dev, w, layers, max(5, args.steps))
     if not args.no_varlen:
         out["varlen_batch"] = varlen_leg(dev, max(5, args.steps))
+    out["measured_hbm"] = hbm_leg(dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_leg(w, layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def hbm_leg(dev, reps=5):
+    """Measured stream-copy rate of a plain library kernel on the same device,
+    as context for the 8 TB/s peak the roofline uses: a 2 GiB device-to-device
+    copy (4 GiB moved), HIP events, best of `reps`."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBs": 2 * n / min(ts) / 1e9, "peak_GBs": HBM_PEAK_GBS,
+            "method": "torch copy_ of 2 GiB (2 GiB read + 2 GiB written), HIP events, best of 5"}
 
 
 def qk_leg(dev, reps):
