@@ -43,7 +43,11 @@ subset search for the Top-p rule, closed-form block-mass identities, a
 hand-worked example, and for the Q/K compression torch's causal softmax and
 logsumexp, the all-zero-score closed form and plain-loop brute force, and for
 the packed batch dense causal attention of each sequence (torch) and a
-per-token brute force.  No function here is "parity unpinned".
+per-token brute force.  The per-row chain pipeline_row is pinned to the
+whole-map path row by row, to the hand-worked example, to torch's attention
+(p = 1, identity head map) and to dense brute force, with planted mistakes
+(a decision on unrounded masses, transposed tile indices) that must fail.
+No function here is "parity unpinned".
 """
 from .mapflow_ref import (  # noqa: F401
     n_blocks, block_mass_row, block_mass, topp_row, decision_masses, topp_select,

@@ -220,7 +220,12 @@ def compress(A, B: int, p: float):
 
 
 def pipeline_row(A, V, W, B: int, p: float, I: int):
-    """Everything for one block row: (mass row, kept columns, tiles, O rows)."""
+    """Everything for one block row: (mass row, kept columns, tiles, O rows).
+
+    The chain of the steps above restricted to block row I: the row's block
+    masses, the Top-p decision on them as fp32 values, the kept tiles and the
+    retrieved output rows.  It equals row I of compress() followed by
+    retrieve()."""
     N = A.shape[1]
     m = block_mass_row(A, B, I)
     kept = topp_row(decision_masses(m), p)

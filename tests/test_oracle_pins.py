@@ -599,3 +599,123 @@ def test_varlen_planted_mistakes_are_detected():
     bad_v = oracle.retrieve_varlen(cu, cr, rp, ci, pool, W, V_shift, B, table)
     for bad in (bad_table, bad_cols, bad_v):
         assert np.abs(bad - ref).max() > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# the per-row pipeline (row oracle of the end-to-end GPU cases)
+# ---------------------------------------------------------------------------
+
+def _pipeline_rows_match(fn, A, V, W, B, p):
+    """True when fn(A, V, W, B, p, I) returns, for every block row I, exactly
+    the row of the whole-map path: block_mass -> topp_select -> build_bsr ->
+    retrieve (mass row, kept set, tiles, O rows)."""
+    N = A.shape[1]
+    mass, kept, rp, ci, vals = oracle.compress(A, B, p)
+    O = oracle.retrieve(rp, ci, vals, W, V, N, B)
+    for I in range(oracle.n_blocks(N, B)):
+        m, k, tiles, O_r = fn(A, V, W, B, p, I)
+        r0, r1 = I * B, min(N, (I + 1) * B)
+        if not np.array_equal(m, mass[I, : I + 1]) or not np.array_equal(k, kept[I]):
+            return False
+        if len(tiles) != rp[I + 1] - rp[I]:
+            return False
+        for t, v in zip(tiles, vals[rp[I]:rp[I + 1]]):
+            if t.dtype != v.dtype or not np.array_equal(t, v):
+                return False
+        if not np.array_equal(O_r, O[r0:r1]):
+            return False
+    return True
+
+
+def _rounding_sensitive_map():
+    """A 2-token, 1-token-block map whose second row's masses differ by 2^-30:
+    as fp32 they tie (0.5, 0.5), so the decision on fp32 masses keeps the
+    lower column; on the fp64 masses the heavier column 1 goes first."""
+    u = 0.5 - 2.0 ** -30
+    A = np.array([[[1.0, 0.0], [u, 1.0 - u]]])
+    W = np.array([[1.5]])
+    V = np.array([[[1.0]], [[-2.0]]])
+    return A, V, W
+
+
+@pytest.mark.parametrize("N,B,p,dtype", [(100, 16, 0.7, np.float64), (64, 16, 0.9, np.float32),
+                                         (37, 32, 0.5, np.float64), (90, 16, 1.0, np.float32),
+                                         (50, 16, 1e-7, np.float64)])
+def test_pipeline_row_is_a_row_of_the_whole_map_path(N, B, p, dtype):
+    rng = np.random.default_rng(N + int(p * 100))
+    A = _random_causal_map(rng, 3, N).astype(dtype)
+    W = rng.standard_normal((4, 3))
+    V = rng.standard_normal((N, 2, 5))
+    assert _pipeline_rows_match(oracle.pipeline_row, A, V, W, B, p)
+
+
+def test_pipeline_row_decides_on_fp32_masses():
+    A, V, W = _rounding_sensitive_map()
+    m, kept, tiles, O = oracle.pipeline_row(A, V, W, 1, 0.5, 1)
+    assert kept.tolist() == [0]                          # the fp32 tie goes to the lower column
+    assert O[0, 0, 0] == pytest.approx(1.5 * (0.5 - 2.0 ** -30) * 1.0, abs=1e-15)
+    assert _pipeline_rows_match(oracle.pipeline_row, A, V, W, 1, 0.5)
+
+
+def test_pipeline_row_handworked_example():
+    with open(os.path.join(GOLDEN, "handworked_n4_b2.json")) as f:
+        g = json.load(f)
+    A, W, V, B = np.array(g["A"]), np.array(g["W"]), np.array(g["V"]), g["B"]
+    for case in g["cases"]:
+        for I in range(2):
+            m, kept, tiles, O = oracle.pipeline_row(A, V, W, B, case["p"], I)
+            assert np.abs(m - np.array(g["mass"])[I, : I + 1]).max() < 1e-12
+            assert kept.tolist() == case["kept"][I]
+            assert np.abs(O[:, 0, 0] - np.array(case["O"])[I * B:(I + 1) * B]).max() < 1e-12
+
+
+def test_pipeline_row_identity_reproduces_dense_attention():
+    w = synth.workload("tiny-f32", N=100, B=16)
+    L = synth.gen_layer(w, map_dtype="f64", return_qk=True)
+    A, V = L["A"].numpy(), L["V"].double().numpy()
+    v = torch.from_numpy(V).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(L["Q"], L["K"], v, is_causal=True)
+    ref = ref.permute(1, 0, 2).numpy()
+    for I in range(w.T):
+        _, kept, _, O = oracle.pipeline_row(A, V, np.eye(w.H_s), w.B, 1.0, I)
+        assert kept.tolist() == list(range(I + 1))
+        r0, r1 = I * w.B, min(w.N, (I + 1) * w.B)
+        assert np.abs(O - ref[r0:r1]).max() < 1e-12 * np.abs(ref).max()
+
+
+def test_pipeline_row_matches_dense_brute_force():
+    rng = np.random.default_rng(21)
+    N, B = 70, 16
+    A = _random_causal_map(rng, 3, N)
+    W = rng.standard_normal((4, 3))
+    V = rng.standard_normal((N, 2, 5))
+    for I in range(oracle.n_blocks(N, B)):
+        _, kept, tiles, O = oracle.pipeline_row(A, V, W, B, 0.8, I)
+        D = np.zeros((3, N, N))                            # only this row's kept blocks
+        for J, t in zip(kept, tiles):
+            c1 = min(N, (J + 1) * B)
+            D[:, I * B:min(N, (I + 1) * B), J * B:c1] = t[:, : min(N, (I + 1) * B) - I * B, : c1 - J * B]
+        ref = _dense_retrieval(D, W, V)[I * B:min(N, (I + 1) * B)]
+        assert np.abs(O - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_pipeline_row_planted_mistakes_are_detected():
+    def unrounded(A, V, W, B, p, I):                     # decides on the fp64 masses
+        m = oracle.block_mass_row(A, B, I)
+        kept = oracle.topp_row(m, p)
+        tiles = [oracle.bsr_tile(A, B, I, int(J)) for J in kept]
+        return m, kept, tiles, oracle.retrieve_row(I, kept, tiles, W, V, A.shape[1], B)
+
+    def swapped(A, V, W, B, p, I):                       # tile indices transposed
+        m = oracle.block_mass_row(A, B, I)
+        kept = oracle.topp_row(oracle.decision_masses(m), p)
+        tiles = [oracle.bsr_tile(A, B, int(J), I) for J in kept]
+        return m, kept, tiles, oracle.retrieve_row(I, kept, tiles, W, V, A.shape[1], B)
+
+    A, V, W = _rounding_sensitive_map()
+    assert not _pipeline_rows_match(unrounded, A, V, W, 1, 0.5)
+    rng = np.random.default_rng(5)
+    A2 = _random_causal_map(rng, 3, 64)
+    W2, V2 = rng.standard_normal((4, 3)), rng.standard_normal((64, 2, 5))
+    assert not _pipeline_rows_match(swapped, A2, V2, W2, 16, 0.9)
+    assert _pipeline_rows_match(oracle.pipeline_row, A2, V2, W2, 16, 0.9)
