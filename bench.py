@@ -6,16 +6,23 @@ B = 64, H_s = 40, H_r = 32, H_kv = 8, d = 128, bf16, p = 0.9), seeded
 synthetic structured sender maps, one distinct sender map per layer.
 
 One step = the whole hot path over all 24 layers, inputs resident in HBM:
-    block mass -> Top-p selection + BSR build -> fused head-mapped retrieval
+    block mass -> Top-p selection + BSR build for every layer, then the fused
+    head-mapped retrieval of every layer
 with no host synchronisation inside the step (BSR capacities are sized in the
-untimed warm-up).  `value` is the metric: fused-retrieval query-tokens/s per
-layer = 24 * N * steps / (sum of retrieval kernel times), timed with HIP
-events on the launch stream.  The line also carries the roofline of the
-retrieval kernel, per-kernel times, and the fp64 CPU oracle timed on a
-bounded sample of block rows of the same workload.
+untimed warm-up).  Compressing all layers first means that no retrieval reads
+tiles that the gather just before it wrote: each layer's compressed state was
+last touched 23 layers earlier (about 10 GB of other traffic), so it comes
+from HBM and not from the 256 MB Infinity Cache.  `value` is the metric:
+fused-retrieval query-tokens/s per layer = 24 * N * steps / (sum of retrieval
+kernel times), timed with HIP events on the launch stream.  The line also
+carries the roofline of the retrieval kernel, per-kernel times, the same
+retrieval timed right after its own gather (the warm, in-pipeline order),
+single-layer retrieval legs for the 8B->3B-like and long-context workloads,
+and the fp64 CPU oracle timed on a bounded sample of block rows.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--no-cpu]
-                    [--no-qk] [--no-varlen] [--no-fanout] [--no-cache] [--copy-ref-mib M]
+                    [--no-qk] [--no-varlen] [--no-fanout] [--no-cache] [--no-configs]
+                    [--copy-ref-mib M]
 """
 from __future__ import annotations
 
@@ -49,6 +56,8 @@ def parse():
                     help="skip the one-sender-several-receivers leg")
     ap.add_argument("--no-cache", action="store_true",
                     help="skip the Block Manager (prefix cache) leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the single-layer 8B->3B and long-context retrieval legs")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference "
                          "kernel for scaling hardware byte counters)")
@@ -160,21 +169,29 @@ def main():
         log(f"copy reference: {args.copy_ref_mib} MiB read + {args.copy_ref_mib} MiB written per launch")
         del src, dst
 
+    def compress(x, evs=None):
+        if evs: evs[0].record(stream)
+        mf.block_mass(x["A"], B, out=x["mass"], workspace=ws_bm)
+        if evs: evs[1].record(stream)
+        mf.topp_select_bsr(x["mass"], x["A"], B, w.p, cap_nnzb=x["nnzb"],
+                           row_ptr=x["rp"], col_idx=x["ci"], vals=x["vals"],
+                           workspace=x["ws"], sync=False)
+        if evs: evs[2].record(stream)
+
+    def retrieve(x, evs=None):
+        if evs: evs[2].record(stream)
+        mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
+                          N, B, out=x["O"], workspace=ws_r)
+        if evs: evs[3].record(stream)
+
     def step(record):
-        for x in layers:
-            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
-            if record: e0.record(stream)
-            mf.block_mass(x["A"], B, out=x["mass"], workspace=ws_bm)
-            if record: e1.record(stream)
-            mf.topp_select_bsr(x["mass"], x["A"], B, w.p, cap_nnzb=x["nnzb"],
-                               row_ptr=x["rp"], col_idx=x["ci"], vals=x["vals"],
-                               workspace=x["ws"], sync=False)
-            if record: e2.record(stream)
-            mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
-                              N, B, out=x["O"], workspace=ws_r)
-            if record:
-                e3.record(stream)
-                rec.append((e0, e1, e2, e3))
+        evs = [[ev(), ev(), ev(), ev(), ev()] if record else None for _ in layers]
+        for x, e in zip(layers, evs):
+            compress(x, e and e[:3])
+        for x, e in zip(layers, evs):
+            retrieve(x, e and [None, None, e[3], e[4]])
+        if record:
+            rec.extend(tuple(e[:2]) + (e[1], e[2], e[3], e[4]) for e in evs)
 
     rec = []
     for _ in range(args.warmup):
@@ -186,9 +203,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - tw0
 
-    t_mass = sum(a.elapsed_time(b) for a, b, c, d in rec) / 1e3
-    t_topp = sum(b.elapsed_time(c) for a, b, c, d in rec) / 1e3
-    t_retr = sum(c.elapsed_time(d) for a, b, c, d in rec) / 1e3
+    # the same retrieval in the warm order: each layer right after its own
+    # gather, whose freshly written tiles partly sit in the Infinity Cache
+    warm = []
+    for _ in range(max(2, args.steps)):
+        for x in layers:
+            compress(x)
+            a, b = ev(), ev()
+            a.record(stream)
+            mf.retrieve_fused(x["rp"], x["ci"], x["vals"], x["nnzb"], x["W"], x["V"],
+                              N, B, out=x["O"], workspace=ws_r)
+            b.record(stream)
+            warm.append((a, b))
+    torch.cuda.synchronize()
+
+    # rec entries: (mass start, mass end, topp start, topp end, retrieve start, retrieve end)
+    t_mass = sum(r[0].elapsed_time(r[1]) for r in rec) / 1e3
+    t_topp = sum(r[2].elapsed_time(r[3]) for r in rec) / 1e3
+    t_retr = sum(r[4].elapsed_time(r[5]) for r in rec) / 1e3
     K = args.steps
     n_retr = K * L
     ms_per_step = wall / K * 1e3
@@ -238,7 +270,8 @@ def main():
         "kernels_ms_per_layer": {"block_mass": t_mass / n_retr * 1e3,
                                  "topp_select_bsr": t_topp / n_retr * 1e3,
                                  "retrieve_fused": t_retr / n_retr * 1e3},
-        "retrieve_fused_launch_us": launch_stats([c.elapsed_time(d) * 1e3 for a, b, c, d in rec]),
+        "retrieve_fused_launch_us": launch_stats([r[4].elapsed_time(r[5]) * 1e3 for r in rec]),
+        "retrieve_fused_after_own_gather_us": launch_stats([a.elapsed_time(b) * 1e3 for a, b in warm]),
         "roofline_kernels": {
             "block_mass_GBs": causal_bytes * K / t_mass / 1e9,
             "topp_select_bsr_GBs": gather_bytes * K / t_topp / 1e9},
@@ -256,10 +289,77 @@ def main():
         out["prefix_cache"] = cache_leg(dev, w, layers, max(5, args.steps))
     if not args.no_varlen:
         out["varlen_batch"] = varlen_leg(dev, max(5, args.steps))
+    if not args.no_configs:
+        out["retrieval_configs"] = {name: single_layer_leg(dev, name, max(10, args.steps))
+                                    for name in ("pair8b3b-f16", "long32k-f16")}
     out["measured_hbm"] = hbm_leg(dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_leg(w, layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def scrub(buf):
+    """Overwrite a 512 MB buffer: afterwards the 256 MB Infinity Cache holds
+    none of the data a timed kernel is about to read."""
+    buf.add_(1)
+
+
+def single_layer_leg(dev, name, reps):
+    """Retrieval of one layer of another workload at its full size: the
+    8B->3B-like pair (N = 4096, B = 64, H_s = 32, H_r = 24, H_kv = 8, fp16,
+    p = 0.95, near-dense maps) or the long-context layer (N = 32768, B = 128,
+    H_s = 32, H_r = 32, H_kv = 8, fp16, p = 0.9).  The layer is generated and
+    compressed (untimed), its dense map freed, and the retrieval timed with HIP
+    events `reps` times, each after a 512 MB scrub; median and spread, and the
+    roofline from the same algorithmic bytes as the headline."""
+    import torch
+    import cross_model_sparse_amd as mf
+    import synth
+    w = synth.workload(name)
+    N, B, T, e = w.N, w.B, w.T, synth.DTYPE_BYTES[w.dtype]
+    t0 = time.time()
+    g = synth.gen_layer(w, device=dev)
+    A = g["A"]
+    W, V = g["W"].to(dev), g["V"].to(dev)
+    mass = mf.block_mass(A, B)
+    rp, ci, vals, nnzb = mf.topp_select_bsr(mass, A, B, w.p)
+    del A, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"{name}: generated and compressed ({time.time() - t0:.1f}s), nnzb {nnzb}")
+    O = torch.empty(N, w.H_r, w.d, dtype=V.dtype, device=dev)
+    buf = torch.zeros(512 << 18, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O)
+    ts = []
+    for _ in range(reps):
+        scrub(buf)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    st = launch_stats(ts)
+    alg = (nnzb * w.H_s * B * B * e + N * w.H_kv * w.d * e + N * w.H_r * w.d * e
+           + 4 * (T + 1 + nnzb) + 4 * w.H_r * w.H_s)
+    flops = 2.0 * nnzb * w.H_r * B * B * (w.H_s + w.d)
+    t = st["median"] * 1e-6
+    rows = np.diff(rp.cpu().numpy())
+    out = {"workload": f"{name}: N={N}, B={B}, H_s={w.H_s}, H_r={w.H_r}, H_kv={w.H_kv}, "
+                       f"d={w.d}, {w.dtype}, p={w.p}, {w.maps} maps",
+           "kernel": mf.retrieve_kernel(vals, V, W, N, B, out=O),
+           "nnzb": nnzb, "density": nnzb / (T * (T + 1) / 2),
+           "kept_per_row": {"min": int(rows.min()), "max": int(rows.max()),
+                            "mean": float(rows.mean())},
+           "retrieve_us": st,
+           "query_tokens_per_s": N / t,
+           "roofline": {"bound": "hbm", "bytes_per_launch": alg, "achieved": alg / t / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": alg / t / 1e9 / HBM_PEAK_GBS,
+                        "mfma_tflops": flops / t / 1e12}}
+    del rp, ci, vals, O, buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def hbm_leg(dev, reps=5):
@@ -630,6 +730,19 @@ def varlen_leg(dev, reps):
     }
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name", read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_leg(w, layers, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of block rows: every
     block row of layer 0 from the last, then layer 1, ... (the same device
@@ -677,7 +790,7 @@ def cpu_leg(w, layers, budget_s):
             break
     tokens = rows * B
     return {"value": tokens / t_retr, "unit": "query-tokens/s per layer",
-            "cores": int(blas_threads), "kind": "oracle",
+            "cores": int(blas_threads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": (f"{rows} block rows ({tokens} query tokens, {blocks} kept blocks) from "
                        f"{used_layers} layer(s), last row first; oracle retrieval "
                        f"{t_retr:.1f} s, oracle compression (host copy + block mass + Top-p "

@@ -117,7 +117,7 @@ __device__ __forceinline__ void transpose8x4(const u32x2 (&x)[8], u32x4 (&y)[4])
 __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
   // 16 bytes per lane from memory straight into LDS at lds_base + 16 * lane
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_base), "v"(g) : "memory");
+               :: "s"(lds_base), "v"(g) : "memory", "m0");
 }
 // A wave-uniform pointer, guaranteed to live in scalar registers.
 __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
@@ -129,7 +129,7 @@ __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
 // Same copy with a wave-uniform base address and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16s(unsigned voff, const void* sbase, unsigned lds_base) {
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
+               :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -404,6 +404,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     return kb + (t >= cnt ? t - cnt : t);
   };
   auto col_ok = [&](int J) { return J >= 0 && J < T; };
+  // valid keys at the start of chunk x of column J: 16, fewer in the chunk
+  // that reaches past N, 0 for an invalid column
+  auto kvalid_of = [&](int x, int J) -> int {
+    if (!col_ok(J)) return 0;
+    const int xc = x < n_chunks ? x : n_chunks - 1;
+    const int rem = N - (J * B + ((xc + sub) & ncc_mask) * kCB);
+    return rem < kCB ? (rem < 0 ? 0 : rem) : kCB;
+  };
   // column of chunk x's block; -1 (never valid) when its page is outside the pool
   auto col_of = [&](int x) -> int {
     const int64_t k = block_of(x);
@@ -488,11 +496,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   };
 
   // head mix of chunk x from tile slot `slot` into mixed-map buffer `ab`;
-  // `keep` = 0 zeroes the chunk (invalid column or padding chunk)
+  // `kvalid` = number of valid keys at the start of the chunk (0: invalid
+  // column or padding chunk); the mixed map is zero from there on, selected
+  // rather than multiplied, so whatever the skipped tile positions hold
+  // (padding past N, a block outside the row's columns) never reaches O
   const int hrow = 4 * rq + (n >> 2);            // tile row of this lane
   const int hkq = n & 3;                         // 4-key quarter of the chunk
   const int hm_off = hrow * 32 + (((hkq >> 1) ^ ((hrow >> 2) & 1)) * 16) + (hkq & 1) * 8;
-  auto head_mix = [&](int slot, bool keep, int ab) {
+  auto key_ok = [&](int kvalid, int t) { return 4 * hkq + t < kvalid; };
+  auto head_mix = [&](int slot, int kvalid, int ab) {
     const unsigned char* st = smem + slot * kStage + hrow * 32 + hkq * 8;
     f32x4 c[4];
 #pragma unroll
@@ -520,13 +532,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     // lane (n, q) holds Ahat[16 hm_mt + 4q + a][hrow][4 hkq + t]; a plane is
     // [32 receivers][16 rows][16 keys], its rows' two 16-byte halves swapped
     // when bit 2 of the row is set
-    const float sc = keep ? 1.f : 0.f;
     unsigned char* dst = smem + kAhatOff + ab * kAhatBuf + hm_off;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int r = 16 * hm_mt + 4 * q + a;
-      const f32x2 v01 = {c[0][a] * sc, c[1][a] * sc};
-      const f32x2 v23 = {c[2][a] * sc, c[3][a] * sc};
+      const f32x2 v01 = {key_ok(kvalid, 0) ? c[0][a] : 0.f, key_ok(kvalid, 1) ? c[1][a] : 0.f};
+      const f32x2 v23 = {key_ok(kvalid, 2) ? c[2][a] : 0.f, key_ok(kvalid, 3) ? c[3][a] : 0.f};
       if constexpr (kBF16) {
         const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector(v01, bf16x2));
         const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector(v23, bf16x2));
@@ -551,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
   // head-mix operand reads, head-mix MFMAs with the next operand's transpose
   // between them, then the A.V MFMAs with the packing of the head-mix result
   // between them.  sched_barrier stops the compiler from regrouping the parts.
-  auto compute = [&](int slot, bool keep, int ab_hm, int ab_av, const u32x4 (&vt)[4], auto&& mid_copy, auto&& step_copy) {
+  auto compute = [&](int slot, int kvalid, int ab_hm, int ab_av, const u32x4 (&vt)[4], auto&& mid_copy, auto&& step_copy) {
     const unsigned char* st = smem + slot * kStage + hrow * 32 + hkq * 8;
     f32x4 c[4];
 #pragma unroll
@@ -587,7 +598,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     }
     // A.V operands
     const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
-    const float sc = keep ? 1.f : 0.f;
     unsigned char* dst = smem + kAhatOff + ab_hm * kAhatBuf + hm_off;
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {
@@ -607,8 +617,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 #pragma unroll
         for (int a = (p * NPL + pl) * 4 / kSteps; a < (p * NPL + pl + 1) * 4 / kSteps; ++a) {
           const int rr = 16 * hm_mt + 4 * q + a;
-          const f32x2 v01 = {c[0][a] * sc, c[1][a] * sc};
-          const f32x2 v23 = {c[2][a] * sc, c[3][a] * sc};
+          const f32x2 v01 = {key_ok(kvalid, 0) ? c[0][a] : 0.f, key_ok(kvalid, 1) ? c[1][a] : 0.f};
+          const f32x2 v23 = {key_ok(kvalid, 2) ? c[2][a] : 0.f, key_ok(kvalid, 3) ? c[3][a] : 0.f};
           if constexpr (kBF16) {
             const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector(v01, bf16x2));
             const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector(v23, bf16x2));
@@ -647,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
     for (int st = 0; st < NSTG; ++st) issue_vals(st, st);
     wait_vm_n((NSTG - 1) * ndv_w);               // V(0) and slice 0 landed
     lds_barrier();
-    head_mix(0, col_ok(J0), 0);
+    head_mix(0, kvalid_of(0, J0), 0);
     wait_vm_n((NSTG - 2) * ndv_w);               // slice 1 landed
     lds_barrier();
   }
@@ -678,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
         if ((d * kSteps) / NDV == step || (step == kSteps - 1 && (d * kSteps) / NDV >= kSteps))
           copy_piece(vsrc, cur, d);
     };
-    compute(s1, u + 1 < n_chunks && col_ok(J1), (u + 1) & 1, u & 1, vt, mid_copy, step_copy);
+    compute(s1, u + 1 < n_chunks ? kvalid_of(u + 1, J1) : 0, (u + 1) & 1, u & 1, vt, mid_copy, step_copy);
     wait_vm_n((NSTG - 2) * ndv_w);               // V(u+1) and slice u+2 landed
     lds_barrier();
     J1 = (!kVar || page_ok(bt, pg_J)) ? Jn_col : -1;

@@ -15,7 +15,11 @@ programmer's job:
   valu_sgpr    no vector-memory instruction reads an SGPR fewer than 5 wait
                states after a VALU instruction (v_readfirstlane, v_readlane)
                wrote it;
-  m0_dma       no LDS DMA directly follows the SALU write of M0 it uses.
+  m0_dma       no LDS DMA directly follows the SALU write of M0 it uses;
+  m0_live      no instruction outside the copy statements reads M0 while the
+               last M0 write before it (in program order) is a copy
+               statement's: a value the compiler keeps in M0 must not be
+               live across them.
 
     python -m cross_model_sparse_amd.isa_check [kernel.hip]
 """
@@ -207,9 +211,48 @@ def _linear_hazards(body):
     return valu_sgpr, m0
 
 
+# Instructions that read M0 without naming it (gfx9 family): indexed register
+# moves, GDS/ordered LDS operations, messages and LDS-direct loads.
+_M0_IMPLICIT = re.compile(r"^(v_movrel|s_movrel|s_sendmsg|ds_gws|ds_ordered|ds_append|ds_consume|"
+                          r"s_set_gpr_idx|v_interp|ds_read_addtid|ds_write_addtid)")
+
+
+def _is_copy_m0(insts, i):
+    """insts[i] is the M0 write of a copy statement: s_mov_b32 m0, sN, then
+    s_nop 0, then the LDS DMA."""
+    return (insts[i].startswith("s_mov_b32 m0,") and i + 2 < len(insts)
+            and insts[i + 1].startswith("s_nop 0") and "lds" in insts[i + 2]
+            and VMEM.match(insts[i + 2].split()[0]) is not None)
+
+
+def _m0_live(body):
+    """Lines that read M0 after a copy statement overwrote it (linear order)."""
+    insts = [s for _, s in body if not s.startswith(".")]
+    lines = [ln for ln, s in body if not s.startswith(".")]
+    writer, bad = None, []
+    i = 0
+    while i < len(insts):
+        s = insts[i]
+        if _is_copy_m0(insts, i):
+            writer = "copy"
+            i += 3
+            continue
+        parts = s.replace(",", " ").split()
+        op, ops = parts[0], parts[1:]
+        reads = _M0_IMPLICIT.match(op) is not None or ("m0" in ops[1:]) or \
+            (op.startswith("s_") and ops[:1] != ["m0"] and "m0" in ops)
+        if ops[:1] == ["m0"] and not op.startswith(("v_", "ds_", "global_", "buffer_")):
+            writer = "compiler"
+        elif reads and writer == "copy":
+            bad.append((lines[i], s))
+        i += 1
+    return bad
+
+
 def check_asm(path: str, pattern: str = "k_retrieve_mfma"):
     """Findings per kernel whose name contains `pattern`: a dict kernel ->
-    {'scratch': bytes, 'inflight': [...], 'valu_sgpr': [...], 'm0_dma': [...]}."""
+    {'scratch': bytes, 'inflight': [...], 'valu_sgpr': [...], 'm0_dma': [...],
+    'm0_live': [...]}."""
     lines = open(path).read().split("\n")
     meta = _metadata(lines)
     out = {}
@@ -219,7 +262,8 @@ def check_asm(path: str, pattern: str = "k_retrieve_mfma"):
         valu_sgpr, m0 = _linear_hazards(body)
         out[name] = {"scratch": meta.get(name, {}).get("private_segment_fixed_size", 0),
                      "vgpr": meta.get(name, {}).get("vgpr_count"),
-                     "inflight": _inflight(body), "valu_sgpr": valu_sgpr, "m0_dma": m0}
+                     "inflight": _inflight(body), "valu_sgpr": valu_sgpr, "m0_dma": m0,
+                     "m0_live": _m0_live(body)}
     return out
 
 
@@ -239,10 +283,12 @@ def main(argv):
         res = check_asm(str(asm))
     bad = 0
     for name, r in sorted(res.items()):
-        n = r["scratch"] + len(r["inflight"]) + len(r["valu_sgpr"]) + len(r["m0_dma"])
+        n = (r["scratch"] + len(r["inflight"]) + len(r["valu_sgpr"]) + len(r["m0_dma"])
+             + len(r["m0_live"]))
         bad += n
         print(f"{name[:60]:60s} vgpr {r['vgpr']} scratch {r['scratch']} inflight "
-              f"{len(r['inflight'])} valu_sgpr {len(r['valu_sgpr'])} m0_dma {len(r['m0_dma'])}")
+              f"{len(r['inflight'])} valu_sgpr {len(r['valu_sgpr'])} m0_dma {len(r['m0_dma'])} "
+              f"m0_live {len(r['m0_live'])}")
     print(f"{len(res)} kernels, {bad} findings")
     return 1 if bad or not res else 0
 

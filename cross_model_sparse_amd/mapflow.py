@@ -169,6 +169,31 @@ def _need_cuda(*ts):
             raise MapflowError(MF_ERR_INVALID, "tensors must be on the GPU")
 
 
+def _check_index(t: torch.Tensor, name: str, min_len: int) -> None:
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, f"{name} must be a contiguous int32 tensor")
+    if t.numel() < min_len:
+        raise MapflowError(MF_ERR_INVALID, f"{name} has {t.numel()} entries, needs >= {min_len}")
+
+
+def _check_bsr(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor, nnzb: int,
+               rows: int | None, pool: bool = False) -> None:
+    """Host-side checks of a BSR state before the kernels see it: nnzb bounds
+    every index the kernels read, so it must fit col_idx and (without a block
+    table) vals; row_ptr has rows + 1 entries (rows None: any length)."""
+    nnzb = int(nnzb)
+    if nnzb < 0:
+        raise MapflowError(MF_ERR_INVALID, "nnzb < 0")
+    _check_index(row_ptr, "row_ptr", 1 if rows is None else rows + 1)
+    if rows is not None and row_ptr.numel() != rows + 1:
+        raise MapflowError(MF_ERR_INVALID, f"row_ptr must have {rows + 1} entries (got {row_ptr.numel()})")
+    _check_index(col_idx, "col_idx", nnzb)
+    if vals.dim() != 4 or vals.shape[2] != vals.shape[3] or not vals.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "vals must be a contiguous [nnzb][H_s][B][B] tensor")
+    if not pool and vals.shape[0] < nnzb:
+        raise MapflowError(MF_ERR_INVALID, f"nnzb = {nnzb} exceeds the {vals.shape[0]} tiles of vals")
+
+
 def abi_version() -> int:
     return load().mf_abi_version()
 
@@ -274,6 +299,9 @@ def retrieve_fused(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Ten
 
     V may be a [N][H_kv][d] tensor or a row-strided view whose last two dims
     are contiguous (e.g. a slice of a fused QKV projection)."""
+    _check_bsr(row_ptr, col_idx, vals, nnzb, -(-N // B))
+    if vals.shape[2] != B:
+        raise MapflowError(MF_ERR_INVALID, f"vals tiles are {vals.shape[2]}x{vals.shape[3]}, B = {B}")
     _need_cuda(row_ptr, col_idx, vals, W, V)
     H_s = vals.shape[1]
     H_r = W.shape[0]
@@ -305,6 +333,7 @@ def retrieve_fused_multi(row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: tor
     receivers: a sequence of (W [H_r][H_s] fp32, V [N][H_kv][d]) pairs; returns
     the list of outputs O_i [N][H_r_i][d] (or fills `outs`)."""
     n = len(receivers)
+    _check_bsr(row_ptr, col_idx, vals, nnzb, -(-N // B))
     _need_cuda(row_ptr, col_idx, vals, *[t for rv in receivers for t in rv])
     H_s = vals.shape[1]
     if outs is None:
@@ -341,14 +370,18 @@ def retrieve_fused_varlen(cu_seqlens: torch.Tensor, cu_rows: torch.Tensor,
     row_ptr covers the R = cu_rows[S] block rows of all sequences; col_idx is
     local to each sequence; vals is the tile pool [n_pages][H_s][B][B], indexed
     through block_table when given.  R, when not given, is len(row_ptr) - 1."""
-    _need_cuda(cu_seqlens, cu_rows, row_ptr, col_idx, vals, W, V)
-    for t, name in ((cu_seqlens, "cu_seqlens"), (cu_rows, "cu_rows"), (row_ptr, "row_ptr")):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise MapflowError(MF_ERR_INVALID, f"{name} must be a contiguous int32 tensor")
+    for t, name in ((cu_seqlens, "cu_seqlens"), (cu_rows, "cu_rows")):
+        _check_index(t, name, 1)
+    _check_bsr(row_ptr, col_idx, vals, nnzb, None, pool=block_table is not None)
+    if block_table is not None:
+        _check_index(block_table, "block_table", int(nnzb))
     if cu_rows.numel() != cu_seqlens.numel():
         raise MapflowError(MF_ERR_INVALID, "cu_rows and cu_seqlens must both have S+1 entries")
     S = cu_seqlens.numel() - 1
     R = row_ptr.numel() - 1 if R is None else int(R)
+    if R < 0 or row_ptr.numel() < R + 1:
+        raise MapflowError(MF_ERR_INVALID, f"row_ptr has {row_ptr.numel()} entries, R = {R} needs R + 1")
+    _need_cuda(cu_seqlens, cu_rows, row_ptr, col_idx, vals, W, V)
     H_s = vals.shape[1]
     H_r = W.shape[0]
     if W.dtype != torch.float32 or not W.is_contiguous() or W.shape[1] != H_s:
@@ -357,8 +390,6 @@ def retrieve_fused_varlen(cu_seqlens: torch.Tensor, cu_rows: torch.Tensor,
         raise MapflowError(MF_ERR_INVALID, "V must be [total][H_kv][d] with contiguous rows")
     if V.dtype != vals.dtype:
         raise MapflowError(MF_ERR_INVALID, "V and vals must share a dtype")
-    if block_table is not None and (block_table.dtype != torch.int32 or not block_table.is_contiguous()):
-        raise MapflowError(MF_ERR_INVALID, "block_table must be a contiguous int32 tensor")
     H_kv, d = V.shape[1], V.shape[2]
     if out is None:
         out = torch.empty(V.shape[0], H_r, d, dtype=V.dtype, device=V.device)

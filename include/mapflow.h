@@ -268,7 +268,10 @@ int mf_retrieve_kernel(int dtype, int H_s, int N, int B, int H_r, int H_kv, int 
  *            (or any BSR of the same layout: row_ptr monotone from 0, col_idx
  *            in [0, T)); `nnzb` is the number of blocks in vals.  Blocks with
  *            a column outside [0, T) and indices k outside [0, nnzb) are
- *            skipped rather than read.
+ *            skipped: they contribute nothing to O.  Tile positions of key
+ *            columns at or beyond N (the padding of a partial last block)
+ *            contribute nothing either, whatever they hold (NaN included).
+ *            Tile values that are used must be finite.
  *  W         device, [H_r][H_s] float32, row-major.
  *  V         device, rows of H_kv*d elements of `dtype` at stride ldV
  *            elements (ldV >= H_kv*d, so V may be a slice of a fused QKV

@@ -374,3 +374,65 @@ def test_header_is_c_and_a_c_program_links_and_runs(tmp_path):
     env = dict(os.environ, LD_LIBRARY_PATH=libdir + os.pathsep + os.environ.get("LD_LIBRARY_PATH", ""))
     out = subprocess.run([str(exe)], env=env, capture_output=True, text=True, timeout=60)
     assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr)
+
+
+def _bsr_args(torch, T=4, nnzb=6, H_s=3, B=16, cap=None):
+    cap = nnzb if cap is None else cap
+    rp = torch.zeros(T + 1, dtype=torch.int32)
+    ci = torch.zeros(cap, dtype=torch.int32)
+    vals = torch.zeros(cap, H_s, B, B, dtype=torch.float16)
+    W = torch.zeros(2, H_s)
+    V = torch.zeros(T * B, 1, 64, dtype=torch.float16)
+    return rp, ci, vals, W, V
+
+
+@pytest.mark.parametrize("case,frag", [
+    ("stale_nnzb", "exceeds the"), ("short_col_idx", "col_idx has"), ("int64_row_ptr", "row_ptr must be"),
+    ("short_row_ptr", "row_ptr"), ("strided_vals", "vals must be"), ("negative_nnzb", "nnzb < 0"),
+    ("tile_size", "vals tiles"),
+])
+def test_binding_checks_bsr_before_launch(case, frag):
+    """The binding refuses a BSR state whose nnzb, index arrays or tiles do not
+    match, before anything reaches the device (host tensors: a check that
+    passed would then fail on 'tensors must be on the GPU')."""
+    import torch
+    rp, ci, vals, W, V = _bsr_args(torch)
+    nnzb, N, B = 6, 64, 16
+    if case == "stale_nnzb":
+        nnzb = 7
+        ci = torch.zeros(7, dtype=torch.int32)
+    elif case == "short_col_idx":
+        ci = ci[:5]
+    elif case == "int64_row_ptr":
+        rp = rp.long()
+    elif case == "short_row_ptr":
+        rp = rp[:4]
+    elif case == "strided_vals":
+        vals = torch.zeros(6, 3, 16, 32, dtype=torch.float16)[..., ::2]
+    elif case == "negative_nnzb":
+        nnzb = -1
+    elif case == "tile_size":
+        B = 32
+        N = 128
+    with pytest.raises(mf.MapflowError, match=frag):
+        mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B)
+
+
+def test_binding_checks_varlen_tables():
+    import torch
+    rp, ci, vals, W, V = _bsr_args(torch)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    cr = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(mf.MapflowError, match="block_table has"):
+        mf.retrieve_fused_varlen(cu, cr, rp, ci, vals, 6, W, V, 16,
+                                 block_table=torch.zeros(5, dtype=torch.int32))
+    with pytest.raises(mf.MapflowError, match="exceeds the"):
+        mf.retrieve_fused_varlen(cu, cr, rp, ci, vals[:5], 6, W, V, 16)
+    with pytest.raises(mf.MapflowError, match="R = 9"):
+        mf.retrieve_fused_varlen(cu, cr, rp, ci, vals, 6, W, V, 16, R=9)
+    # a pool smaller than nnzb is fine with a table (pages index the pool)
+    with pytest.raises(mf.MapflowError, match="on the GPU"):
+        mf.retrieve_fused_varlen(cu, cr, rp, ci, vals[:2], 6, W, V, 16,
+                                 block_table=torch.zeros(6, dtype=torch.int32))
+    with pytest.raises(mf.MapflowError, match="on the GPU"):
+        mf.retrieve_fused(rp, ci, vals, 6, W, V, 64, 16)

@@ -66,9 +66,35 @@ def test_checker_flags_planted_mistakes(tmp_path):
     assert [s for _, s in r["inflight"]] == ["v_add_u32_e32 v40, v20, v41"]
 
 
+M0_LIVE = """
+_Zk_retrieve_mfma_demo:
+\ts_mov_b32 m0, s12
+\ts_mov_b32 m0, s13
+\ts_nop 0
+\tglobal_load_lds_dwordx4 v31, s[8:9]
+\tv_movrel_b32_e32 v1, v2
+\ts_mov_b32 m0, -1
+\tv_movrel_b32_e32 v3, v4
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+\t.amdhsa_kernel x
+    .name:           _Zk_retrieve_mfma_demo
+    .private_segment_fixed_size: 0
+    .vgpr_count:     64
+"""
+
+
+def test_checker_flags_m0_live_across_a_copy(tmp_path):
+    r = _check_text(tmp_path, M0_LIVE)
+    # the first v_movrel reads the copy's M0; the second follows a fresh write
+    assert [s for _, s in r["m0_live"]] == ["v_movrel_b32_e32 v1, v2"]
+
+
 def test_checker_accepts_the_fixed_forms(tmp_path):
     r = _check_text(tmp_path, CLEAN)
     assert r["scratch"] == 0 and not r["valu_sgpr"] and not r["m0_dma"] and not r["inflight"]
+    assert not r["m0_live"]
 
 
 # one instantiation per code shape: bf16/fp16, 1 or 2 receiver pairs, 2 or 3
@@ -96,3 +122,4 @@ def test_retrieve_kernels_have_no_hazards(retrieve_asm, tag):
     assert not r["valu_sgpr"], r["valu_sgpr"][:3]
     assert not r["m0_dma"], r["m0_dma"][:3]
     assert not r["inflight"], r["inflight"][:3]
+    assert not r["m0_live"], r["m0_live"][:3]
