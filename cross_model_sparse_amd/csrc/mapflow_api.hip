@@ -4,9 +4,21 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "mf_internal.h"
+
+// Fixed scratch of mf_topp_select_bsr_noalloc: the selection's kept[T][T] and
+// count[T] int32 arrays for up to kNoAllocMaxT block rows.  Each GPU the
+// library runs on holds its own copy for the life of the process.  Host code
+// never uses this name as an address: the per-device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+namespace {
+constexpr int kNoAllocMaxT = 1024;
+constexpr size_t kNoAllocScratchBytes = ((size_t)kNoAllocMaxT * kNoAllocMaxT + kNoAllocMaxT) * 4;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace mf {
 
@@ -58,6 +70,35 @@ int check_geom(const char* fn, int dtype, int H_s, int N, int B) {
   if (N < 1) return fail(MF_ERR_INVALID, f + fmt("N must be >= 1 (got %lld)", N));
   if (!valid_block(B)) return fail(MF_ERR_INVALID, f + fmt("B must be 16, 32, 64 or 128 (got %lld)", B));
   if (H_s < 1 || H_s > 64) return fail(MF_ERR_INVALID, f + fmt("H_s must be in [1, 64] (got %lld)", H_s));
+  return MF_OK;
+}
+
+}  // namespace
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device and cached.
+int noalloc_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return mf::hip_check(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return mf::fail(MF_ERR_UNSUPPORTED, std::string(fn) + fmt(": device index %lld >= 64", dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return mf::hip_check(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                           (std::string(fn) + " scratch address").c_str());
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
   return MF_OK;
 }
 
@@ -156,6 +197,32 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
     return mf::fail(MF_ERR_CAPACITY, std::string(fn) + fmt(": nnzb = %lld exceeds cap_nnzb = %lld",
                                                            nnzb, cap_nnzb));
   return MF_OK;
+}
+
+int mf_topp_select_bsr_noalloc(const float* mass, const void* A, int dtype, int H_s, int N, int B,
+                               float p, int32_t* row_ptr, int32_t* col_idx, void* vals,
+                               int64_t cap_nnzb, void* stream) {
+  const char* fn = "mf_topp_select_bsr_noalloc";
+  int st = check_geom(fn, dtype, H_s, N, B);
+  if (st != MF_OK) return st;
+  if (!mass || !A || !row_ptr) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null pointer");
+  if (cap_nnzb < 0) return mf::fail(MF_ERR_INVALID, std::string(fn) + ": cap_nnzb < 0");
+  if (cap_nnzb > 0 && (!col_idx || !vals))
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": null col_idx/vals with cap_nnzb > 0");
+  if (!(p > 0.0f && p <= 1.0f))  // also rejects NaN
+    return mf::fail(MF_ERR_INVALID, std::string(fn) + ": p must be in (0, 1]");
+  const int T = mf::blocks_of(N, B);
+  if (T > kNoAllocMaxT)
+    return mf::fail(MF_ERR_UNSUPPORTED,
+                    std::string(fn) + fmt(": T = %lld block rows exceeds the %lld that the fixed scratch "
+                                          "holds (use mf_topp_select_bsr with a workspace)",
+                                          T, kNoAllocMaxT));
+  void* ws = nullptr;
+  st = noalloc_scratch(fn, &ws);
+  if (st != MF_OK) return st;
+  return mf::hip_check(mf::launch_topp_bsr(mass, A, dtype, H_s, N, B, p, row_ptr, col_idx, vals,
+                                           cap_nnzb, ws, (hipStream_t)stream),
+                       "mf_topp_select_bsr_noalloc launch");
 }
 
 // Shape checks shared by the calls that read Q and K.

@@ -24,7 +24,7 @@ _DTYPE_CODE = {torch.float32: MF_F32, torch.float16: MF_F16, torch.bfloat16: MF_
 
 EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mass",
             "mf_block_mass_ws_bytes", "mf_block_mass_ws",
-            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_row_lse",
+            "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_topp_select_bsr_noalloc", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk",
             "mf_lse_block_mass_qk_workspace_bytes", "mf_lse_block_mass_qk", "mf_topp_select_bsr_qk",
             "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
@@ -78,6 +78,9 @@ def load() -> ctypes.CDLL:
     L.mf_topp_select_bsr.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_f, c_vp,
                                      c_vp, c_vp, c_i64, ctypes.POINTER(c_i64), c_vp,
                                      c_sz, c_vp]
+    L.mf_topp_select_bsr_noalloc.restype = c_int
+    L.mf_topp_select_bsr_noalloc.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_f, c_vp,
+                                             c_vp, c_vp, c_i64, c_vp]
     L.mf_row_lse.restype = c_int
     L.mf_row_lse.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp]
     L.mf_block_mass_qk_workspace_bytes.restype = c_sz
@@ -273,6 +276,27 @@ def topp_select_bsr(mass: torch.Tensor, A: torch.Tensor, B: int, p: float,
     _check(st, int(n.value))
     nnzb = int(n.value) if sync else None
     return row_ptr, col_idx, vals, nnzb
+
+
+def topp_select_bsr_noalloc(mass: torch.Tensor, A: torch.Tensor, B: int, p: float,
+                            row_ptr: torch.Tensor, col_idx: torch.Tensor, vals: torch.Tensor,
+                            cap_nnzb: int, stream=None) -> None:
+    """Top-p selection and BSR build into the caller's buffers without any
+    allocation (mf_topp_select_bsr_noalloc: fixed library scratch, T <= 1024,
+    no synchronisation; nnzb is row_ptr[T]).  Calls that overlap on one GPU
+    share the scratch and must not be issued."""
+    H_s, N, N2 = A.shape
+    if N2 != N or not A.is_contiguous():
+        raise MapflowError(MF_ERR_INVALID, "A must be a contiguous [H_s][N][N] tensor")
+    T = -(-N // B)
+    _check_index(row_ptr, "row_ptr", T + 1)
+    _check_index(col_idx, "col_idx", int(cap_nnzb))
+    if vals.dtype != A.dtype or not vals.is_contiguous() or vals.shape[0] < cap_nnzb:
+        raise MapflowError(MF_ERR_INVALID, "vals must be a contiguous [cap][H_s][B][B] tensor of A's dtype")
+    _need_cuda(mass, A, row_ptr, col_idx, vals)
+    _check(load().mf_topp_select_bsr_noalloc(_ptr(mass), _ptr(A), _dcode(A), H_s, N, B, float(p),
+                                             _ptr(row_ptr), _ptr(col_idx), _ptr(vals), int(cap_nnzb),
+                                             _stream(stream)))
 
 
 def retrieve_kernel(vals: torch.Tensor, V: torch.Tensor, W: torch.Tensor, N: int, B: int,

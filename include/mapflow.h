@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 5
+#define MF_ABI_VERSION 6
 
 typedef enum {
   MF_OK = 0,
@@ -151,6 +151,32 @@ int mf_topp_select_bsr(const float* mass, const void* A, int dtype, int H_s,
                        int32_t* col_idx, void* vals, int64_t cap_nnzb,
                        int64_t* nnzb_out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * mf_topp_select_bsr for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Computes exactly what mf_topp_select_bsr(..., nnzb_out = NULL,
+ * ...) computes (same kernels, bitwise the same row_ptr, col_idx and vals),
+ * with the selection's scratch taken from a fixed device array inside the
+ * library instead of a caller workspace.  It allocates nothing and does not
+ * synchronise: read row_ptr[T] for nnzb; when nnzb > cap_nnzb, col_idx and
+ * vals are left untouched, as in mf_topp_select_bsr.
+ *  Limit: T = ceil(N/B) <= 1024 block rows (the array holds kept[T][T] and
+ *  count[T] int32, 4.2 MB; each GPU the library runs on holds its own copy
+ *  until the process ends).  The array's device address is looked up once
+ *  per device on the first call there, with that device current; the calling
+ *  thread's current device must be the one `stream` runs on.
+ *  Every call on one GPU uses the same array: calls that overlap in time on
+ *  one GPU (different streams, or different host threads) race and must not
+ *  be issued.  Nothing in the array needs clearing between calls (every entry
+ *  a call reads, it has written itself first).
+ *  Errors: those of mf_topp_select_bsr (no workspace or nnzb_out arguments),
+ *  and MF_ERR_UNSUPPORTED when T > 1024.
+ */
+int mf_topp_select_bsr_noalloc(const float* mass, const void* A, int dtype, int H_s,
+                               int N, int B, float p, int32_t* row_ptr,
+                               int32_t* col_idx, void* vals, int64_t cap_nnzb,
+                               void* stream);
 
 /*
  * Compression without a dense map (article, third section, first component:

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mf.abi_version() == 5
+    assert mf.abi_version() == 6
     for st in range(5):
         assert L.mf_status_string(st)
     assert b"unknown" in L.mf_status_string(99)
@@ -436,3 +436,18 @@ def test_binding_checks_varlen_tables():
                                  block_table=torch.zeros(6, dtype=torch.int32))
     with pytest.raises(mf.MapflowError, match="on the GPU"):
         mf.retrieve_fused(rp, ci, vals, 6, W, V, 64, 16)
+
+
+def test_noalloc_rejects_before_any_launch(L):
+    """Argument checks of mf_topp_select_bsr_noalloc run on the host: more block
+    rows than its fixed scratch holds is MF_ERR_UNSUPPORTED, bad arguments are
+    MF_ERR_INVALID, and none of them touches the GPU."""
+    fake = 1 << 40
+    f = L.mf_topp_select_bsr_noalloc
+    assert f(fake, fake, 2, 40, 1025 * 64, 64, ctypes.c_float(0.9), fake, fake, fake, 10, None) == 2
+    assert "1024" in _last(L)
+    assert f(fake, fake, 2, 40, 1024 * 64, 64, ctypes.c_float(1.5), fake, fake, fake, 10, None) == 1
+    assert f(None, fake, 2, 40, 4096, 64, ctypes.c_float(0.9), fake, fake, fake, 10, None) == 1
+    assert f(fake, fake, 2, 40, 4096, 64, ctypes.c_float(0.9), fake, None, None, 10, None) == 1
+    assert f(fake, fake, 2, 40, 4096, 64, ctypes.c_float(0.9), fake, fake, fake, -1, None) == 1
+    assert f(fake, fake, 9, 40, 4096, 64, ctypes.c_float(0.9), fake, fake, fake, 10, None) == 1
