@@ -65,6 +65,7 @@
 // so the compressed state of many sequences (or layers) can live in one
 // allocation; a page outside the pool contributes nothing.
 #include <algorithm>
+#include <type_traits>
 
 #include "mf_internal.h"
 
@@ -728,6 +729,427 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 }
 
 // ---------------------------------------------------------------------------
+// MFMA kernel, pair-stage form (B >= 32)
+// ---------------------------------------------------------------------------
+//
+// The same work items, head-mix plan and A.V tiling as k_retrieve_mfma, with
+// the memory traffic reorganised:
+//   * tile slices are copied as key pairs: one 1 KB copy moves one sender
+//     head's [16 rows][32 keys], i.e. 64 contiguous bytes of each tile row
+//     (half a 128-byte line instead of a quarter), into one of two pair
+//     stages [head slot][16 rows][32 keys]; a pair serves two consecutive
+//     16-key phases;
+//   * the V rows of the next chunk come straight into registers (eight 8-byte
+//     loads per lane, issued at the start of the phase before their use), so
+//     LDS holds only tile pairs and the two mixed-map buffers.
+// Pair P goes into stage P % 2 once the head mix of the previous occupant's
+// last chunk has passed a barrier: it is issued between the A.V MFMAs of
+// phase 2P-3 and waited for at the end of phase 2P-2.
+
+// 8 bytes per lane from memory into a register pair: wave-uniform base and a
+// 32-bit per-lane byte offset, or a per-lane address.  The registers receive
+// the data asynchronously; they are read only after wait_vm_regs() has
+// retired the load.
+__device__ __forceinline__ void vld8s(u32x2& dst, unsigned voff, const void* sbase) {
+  asm volatile("s_nop 4\n\tglobal_load_dwordx2 %0, %1, %2"
+               : "=v"(dst) : "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
+}
+__device__ __forceinline__ void vld8(u32x2& dst, const void* g) {
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(dst) : "v"(g) : "memory");
+}
+// s_waitcnt vmcnt(N) that the eight V registers depend on, so that no read of
+// them is scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm_regs(u32x2 (&x)[8]) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                 "+v"(x[6]), "+v"(x[7])
+               : "n"(N) : "memory");
+}
+
+template <bool kBF16, int NCH, int NPAIR, bool kVar>
+__global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N, int B,
+    int lg_ncc, const float* __restrict__ W, int H_r, int RPW, int G,
+    const unsigned short* __restrict__ V, int64_t ldV,
+    unsigned short* __restrict__ O, int64_t ldO, int RG, Batch bt,
+    const int32_t* __restrict__ cu_rows, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ block_table, int R) {
+  using Plan = HmPlan<kBF16, NCH>;
+  constexpr int NBOP = Plan::NBOP;
+  constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
+  constexpr int kPieces = 8 * NCH;                 // 1 KB copies per pair: one per head slot
+  constexpr int kHeadPair = 1024;                  // bytes: one head of one pair stage
+  constexpr int kStage = kPieces * kHeadPair;      // [head slot][16 rows][32 keys]
+  constexpr int kAhatOff = 2 * kStage;
+  constexpr int kAhatBuf = NPL * kPlane;
+  constexpr int kUsed = kAhatOff + 2 * kAhatBuf;
+  constexpr int kSmem = kUsed > kWaves * kOutSlot ? kUsed : kWaves * kOutSlot;
+  static_assert(kSmem <= 160 * 1024, "LDS budget");
+  static_assert(NPAIR == 1 || NPAIR == 2, "receiver pairs per wavefront");
+  static_assert(NCH <= 6, "copies per wavefront per pair");
+  __shared__ __align__(16) unsigned char smem[kSmem];
+
+  const int subs = B / kRows;
+  int bid = blockIdx.x;
+  if constexpr (kVar) {
+    if (bt.n_recv > 1) {
+      const int local = bid >> 3;
+      const Recv& rc = bt.recv[local % bt.n_recv];
+      bid = (bid & 7) | ((local / bt.n_recv) << 3);
+      W = rc.W;
+      H_r = rc.H_r;
+      RPW = rc.RPW;
+      G = rc.G;
+      V = reinterpret_cast<const unsigned short*>(rc.V);
+      ldV = rc.ldV;
+      O = reinterpret_cast<unsigned short*>(rc.O);
+      ldO = rc.ldO;
+    }
+  }
+  int Ig, sub;
+  if (!item_of(bid, subs, R, RG, &Ig, &sub)) return;
+  RowView rv;
+  if (!row_view<kVar>(bt, cu_rows, cu_seqlens, Ig, N, B, rv)) return;
+  const int I = rv.I;
+  const int T = rv.T;
+  N = rv.N;
+  V += rv.tok0 * ldV;
+  O += rv.tok0 * ldO;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+
+  // ---- head-mix role and W operands (as in k_retrieve_mfma) ----------------
+  const int hm_mt = wave >> 2;
+  const int rq = wave & 3;
+  u32x4 wop[NBOP][2];
+#pragma unroll
+  for (int b = 0; b < NBOP; ++b)
+#pragma unroll
+    for (int w = 0; w < Plan::nw(b); ++w) {
+      const int r = 16 * hm_mt + n;
+      const int c = Plan::chunk(b, q);
+      const int hf = Plan::half(b, w, q);
+      unsigned short hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = 8 * c + j;
+        const bool ok = c >= 0 && r < H_r && s < H_s;
+        const float x = W[ok ? r * H_s + s : 0];
+        const float xv = ok ? x : 0.f;
+        if constexpr (kBF16) {
+          const unsigned short hi = bf16_bits(xv);
+          hv[j] = hf == 0 ? hi : bf16_bits(xv - bf16_to_f32(hi));
+        } else {
+          hv[j] = f32_to_f16(xv);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wop[b][w][j] = (unsigned)hv[2 * j] | ((unsigned)hv[2 * j + 1] << 16);
+    }
+#pragma unroll
+  for (int b = 0; b < NBOP; ++b) asm volatile("" :: "v"(wop[b][0]));
+
+  f32x16 acc[NPAIR][4];
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[p][dt] = f32x16{};
+
+  const int rbeg = wave * RPW;
+  const int g = rbeg / G;
+  int64_t kb = row_ptr[Ig], ke = row_ptr[Ig + 1];
+  kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
+  ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
+  const int lg_npb = lg_ncc - 1;                 // pairs per block: B / 32
+  const int npb_mask = (1 << lg_npb) - 1;
+  const int cnt = (int)(ke - kb);
+  const int n_chunks = cnt << lg_ncc;
+  const int64_t tile = (int64_t)B * B;
+  const int rot = cnt > 0 ? cnt - 1 - I % cnt : 0;
+  auto block_of = [&](int x) -> int64_t {        // kept block of chunk x (clamped)
+    x = x < n_chunks ? x : n_chunks - 1;
+    const int t = (x >> lg_ncc) + rot;
+    return kb + (t >= cnt ? t - cnt : t);
+  };
+  auto col_ok = [&](int J) { return J >= 0 && J < T; };
+  // key offset of chunk x in its block: the pair's staggered position, then
+  // the chunk's half of it (the row slices of one block row take the block's
+  // pairs in staggered order)
+  auto key_off = [&](int x) -> int {
+    x = x < n_chunks ? x : n_chunks - 1;
+    return ((((x >> 1) + sub) & npb_mask) << 5) + ((x & 1) << 4);
+  };
+  auto kvalid_of = [&](int x, int J) -> int {
+    if (!col_ok(J)) return 0;
+    const int rem = N - (J * B + key_off(x));
+    return rem < kCB ? (rem < 0 ? 0 : rem) : kCB;
+  };
+  auto col_of = [&](int x) -> int {
+    const int64_t k = block_of(x);
+    if constexpr (!kVar) return col_idx[k];
+    else return page_of<kVar>(bt, block_table, k) >= 0 ? col_idx[k] : -1;
+  };
+
+  // Pair-stage layout: head slot hs holds 16 rows of 64 bytes; the four
+  // 16-byte quarters of row r sit in the order quarter ^ swz(r, hs / 8), so
+  // that one head-mix read (four sender groups x four rows x 32 bytes) spreads
+  // over all LDS banks instead of meeting itself 8 times on half of them.
+  auto swz = [](int r, int grp) { return (grp + (r >> 1)) & 3; };
+  // tile-pair copy d of this wavefront: head slot hs = wave + 8d; lane -> the
+  // 16 bytes at LDS offset 16*lane of the slot, i.e. tile row lane/4 and
+  // quarter (lane%4) ^ swz
+  unsigned head_off[NCH];
+#pragma unroll
+  for (int d = 0; d < NCH; ++d) {
+    const int hs = wave + kWaves * d;
+    const int s = hs < H_s ? hs : H_s - 1;      // padding slots get a real head (zero weight)
+    const int row = lane >> 2;
+    const int quarter = (lane & 3) ^ swz(row, hs >> 3);
+    head_off[d] = (unsigned)((s * tile + (int64_t)(sub * kRows + row) * B + quarter * 8) * 2);
+  }
+  const unsigned smem_lds = lds_addr(smem);
+  // copies of pair P (its first chunk 2P) into stage P % 2; with a block table
+  // the page is passed in (loaded a phase ahead)
+  auto issue_pair = [&](int P, int64_t pg, int d) {
+    const int x = 2 * P;
+    const unsigned short* src;
+    if constexpr (!kVar) src = vals + block_of(x) * H_s * tile + key_off(x);
+    else src = vals + (page_ok(bt, pg) ? pg : 0) * H_s * tile + key_off(x);
+    dma16s(head_off[d], src, smem_lds + (P & 1) * kStage + (wave + kWaves * d) * kHeadPair);
+  };
+  auto pair_page = [&](int P) -> int64_t {
+    if constexpr (!kVar) return 0;
+    else return page_of<kVar>(bt, block_table, block_of(2 * P));
+  };
+
+  // V rows of chunk x for this wavefront's KV head g, straight into registers:
+  // lane -> keys 8*(lane/32)+j (j = 0..7) of columns 4*(lane%32)..+3.  A
+  // chunk reaching past row N (only the last of a partial block) reads row
+  // N-1 for the missing keys; their mixed-map weights are zero.
+  const unsigned v_off = (unsigned)(((int64_t)(8 * (lane >> 5)) * ldV + g * kD + 4 * (lane & 31)) * 2);
+  const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
+  u32x2 xv[8];
+  auto issue_v = [&](int x, int J) {
+    const int key0 = (col_ok(J) ? J : 0) * B + key_off(x);
+    if (key0 + kCB <= N) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vld8s(xv[j], v_off, V + (int64_t)(key0 + j) * ldV);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = key0 + 8 * (lane >> 5) + j;
+        vld8(xv[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
+      }
+    }
+  };
+
+  // ---- head mix ---------------------------------------------------------------
+  const int hrow = 4 * rq + (n >> 2);
+  const int hkq = n & 3;
+  const int hm_off = hrow * 32 + (((hkq >> 1) ^ ((hrow >> 2) & 1)) * 16) + (hkq & 1) * 8;
+  auto key_ok = [&](int kvalid, int t) { return 4 * hkq + t < kvalid; };
+  // operand base of chunk x: its pair's stage and this lane's row; the
+  // quarter (16-key half of the pair, 8-key half of that) is placed by
+  // read_hm, which knows the sender group
+  auto hm_base = [&](int x) -> const unsigned char* {
+    return smem + ((x >> 1) & 1) * kStage + hrow * 64;
+  };
+  auto pack_row = [&](unsigned char* dst, const f32x4 (&c)[4], int a, int kvalid) {
+    const int rr = 16 * hm_mt + 4 * q + a;
+    const f32x2 v01 = {key_ok(kvalid, 0) ? c[0][a] : 0.f, key_ok(kvalid, 1) ? c[1][a] : 0.f};
+    const f32x2 v23 = {key_ok(kvalid, 2) ? c[2][a] : 0.f, key_ok(kvalid, 3) ? c[3][a] : 0.f};
+    if constexpr (kBF16) {
+      const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_convertvector(v01, bf16x2));
+      const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_convertvector(v23, bf16x2));
+      const f32x2 r01 = {v01[0] - __uint_as_float(h01 << 16), v01[1] - __uint_as_float(h01 & 0xffff0000u)};
+      const f32x2 r23 = {v23[0] - __uint_as_float(h23 << 16), v23[1] - __uint_as_float(h23 & 0xffff0000u)};
+      const unsigned l01 = __builtin_bit_cast(unsigned, __builtin_convertvector(r01, bf16x2));
+      const unsigned l23 = __builtin_bit_cast(unsigned, __builtin_convertvector(r23, bf16x2));
+      *reinterpret_cast<u32x2*>(dst + rr * 512) = u32x2{h01, h23};
+      *reinterpret_cast<u32x2*>(dst + kPlane + rr * 512) = u32x2{l01, l23};
+    } else {
+      *reinterpret_cast<u32x2*>(dst + rr * 512) =
+          u32x2{pack_f16x2(v01[0], v01[1]), pack_f16x2(v23[0], v23[1])};
+    }
+  };
+  auto hm_mfmas = [&](const u32x4 (&y)[4], int b, f32x4 (&c)[4]) {
+#pragma unroll
+    for (int w = 0; w < Plan::nw(b); ++w)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if constexpr (kBF16)
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wop[b][w]), as_bf16x8(y[t]), c[t], 0, 0, 0);
+        else
+          c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wop[b][w]), as_f16x8(y[t]), c[t], 0, 0, 0);
+      }
+  };
+  // operands of group b for chunk half xh (x & 1): 4 keys x 8 sender heads
+  auto read_hm = [&](const unsigned char* st, int xh, int b, u32x2 (&x)[8]) {
+    const int ch = Plan::chunk(b, q) < 0 ? 0 : Plan::chunk(b, q);
+    const int quarter = ((xh << 1) | (hkq >> 1)) ^ swz(hrow, ch);
+    const unsigned char* sp = st + quarter * 16 + (hkq & 1) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x2*>(sp + (8 * ch + j) * kHeadPair);
+  };
+  // prologue form: head mix of chunk x into mixed-map buffer ab
+  auto head_mix = [&](int x, int kvalid, int ab) {
+    const unsigned char* st = hm_base(x);
+    f32x4 c[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NBOP; ++b) {
+      u32x2 x8[8];
+      u32x4 y[4];
+      read_hm(st, x & 1, b, x8);
+      transpose8x4(x8, y);
+      hm_mfmas(y, b, c);
+    }
+    unsigned char* dst = smem + kAhatOff + ab * kAhatBuf + hm_off;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) pack_row(dst, c, a, kvalid);
+  };
+
+  const int am = lane & 31;
+  const int a_off = (am & 15) * 32 + (((lane >> 5) ^ ((am >> 2) & 1)) * 16);
+  constexpr int kSteps = NPAIR * NPL;            // A.V steps that can carry a copy
+
+  // One phase: head-mix operand reads and MFMAs of chunk x1 (next operand's
+  // transpose between them), then the A.V MFMAs of the current chunk with the
+  // packing of the head-mix result and the phase's tile-pair copies between
+  // them.
+  auto compute = [&](int x1, int kvalid, int ab_hm, int ab_av, const u32x4 (&vt)[4], auto&& step_copy) {
+    const unsigned char* st = hm_base(x1);
+    f32x4 c[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x2 x[8];
+    read_hm(st, x1 & 1, 0, x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NBOP; ++b) {
+      u32x4 y[4];
+      transpose8x4(x, y);
+      if (b + 1 < NBOP) read_hm(st, x1 & 1, b + 1, x);
+      hm_mfmas(y, b, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
+    unsigned char* dst = smem + kAhatOff + ab_hm * kAhatBuf + hm_off;
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      const int r = rbeg + 2 * p + (am >> 4);
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        const u32x4 a4 = *reinterpret_cast<const u32x4*>(asrc + pl * kPlane + r * 512);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          if constexpr (kBF16)
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a4), as_bf16x8(vt[dt]), acc[p][dt], 0, 0, 0);
+          else
+            acc[p][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a4), as_f16x8(vt[dt]), acc[p][dt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int a = (p * NPL + pl) * 4 / kSteps; a < (p * NPL + pl + 1) * 4 / kSteps; ++a)
+          pack_row(dst, c, a, kvalid);
+        step_copy(p * NPL + pl);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- pipeline ---------------------------------------------------------------
+  int J1 = 0;                                    // column of chunk u+1
+  int64_t pg_next = 0;                           // table page of the next pair to copy
+  if (n_chunks > 0) {
+    const int J0 = col_of(0);
+    J1 = col_of(1);
+    issue_v(0, J0);
+    const int64_t pg0 = pair_page(0), pg1 = pair_page(1);
+#pragma unroll
+    for (int d = 0; d < NCH; ++d) issue_pair(0, pg0, d);
+#pragma unroll
+    for (int d = 0; d < NCH; ++d) issue_pair(1, pg1, d);
+    wait_vm_regs<NCH>(xv);                       // V(0) and pair 0 landed
+    lds_barrier();
+    head_mix(0, kvalid_of(0, J0), 0);
+    lds_barrier();
+    pg_next = pair_page(2);
+  }
+  // Two phases per iteration (n_chunks is even for B >= 32), so that which
+  // phases copy a pair and how many copies each wait leaves in flight are
+  // fixed in the code: the even phase copies nothing and waits for
+  // everything, the odd phase copies pair (u+3)/2 and waits for all but those
+  // NCH copies.
+  auto phase = [&](int u, auto odd_tag) {
+    constexpr bool kOdd = decltype(odd_tag)::value;
+    const int64_t kn = block_of(u + 2);          // column of chunk u+2: used after the barrier
+    const int Jn_col = col_idx[kn];
+    int64_t pg_J = 0;
+    if constexpr (kVar) pg_J = page_raw<kVar>(block_table, col_idx, kn);
+    u32x4 vt[4];
+    transpose8x4(xv, vt);                        // V(u)
+    issue_v(u + 1, J1);                          // V(u+1)
+    // odd phase: pair (u+3)/2 into the stage whose last chunk was head-mixed
+    // in the previous phase, right behind V(u+1): loads return in issue
+    // order, so V goes first, and the pair gets two whole phases
+    const int P = (u + 3) >> 1;
+    if constexpr (kOdd) {
+#pragma unroll
+      for (int d = 0; d < NCH; ++d) issue_pair(P, pg_next, d);
+    }
+    auto step_copy = [&](int) {};
+    compute(u + 1, u + 1 < n_chunks ? kvalid_of(u + 1, J1) : 0, (u + 1) & 1, u & 1, vt, step_copy);
+    if constexpr (kOdd) {
+      wait_vm_regs<NCH>(xv);                     // V(u+1) landed (this phase's pair in flight)
+      if constexpr (kVar) pg_next = pair_page(P + 1);
+    } else {
+      wait_vm_regs<0>(xv);                       // V(u+1) and the pair copied last phase
+    }
+    lds_barrier();
+    J1 = (!kVar || page_ok(bt, pg_J)) ? Jn_col : -1;
+  };
+  for (int u = 0; u < n_chunks; u += 2) {
+    phase(u, std::false_type{});
+    phase(u + 1, std::true_type{});
+  }
+  wait_vm<0>();
+  lds_barrier();
+
+  // ---- store through LDS (as in k_retrieve_mfma) ------------------------------
+  unsigned short* ot = reinterpret_cast<unsigned short*>(smem + wave * kOutSlot);
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p) {
+    if (p) lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      unsigned short h[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) h[dt] = kBF16 ? bf16_bits(acc[p][dt][e]) : f32_to_f16(acc[p][dt][e]);
+      *reinterpret_cast<u32x2*>(ot + ((m & 15) * 2 + (m >> 4)) * kD + 4 * am) =
+          u32x2{(unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16)};
+    }
+    lds_barrier();
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const int c16 = pass * 64 + lane;
+      const int i = c16 >> 5, rp = (c16 >> 4) & 1, d8 = (c16 & 15) * 8;
+      const int64_t grow = (int64_t)I * B + sub * kRows + i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + (i * 2 + rp) * kD + d8);
+      if (2 * p + rp < RPW && grow < N)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)(rbeg + 2 * p + rp) * kD + d8));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Plain kernel
 // ---------------------------------------------------------------------------
 
@@ -864,6 +1286,48 @@ int launch_mfma_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
   return mf::hip_check(hipGetLastError(), "k_retrieve_mfma launch");
 }
 
+// The pair-stage kernel, B >= 32 (same arguments and cases as launch_mfma_p).
+template <bool kBF16, int NPAIR, bool kGeneral = false>
+int launch_pair_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
+                  const int32_t* col_idx, const unsigned short* vals, int64_t nnzb,
+                  int H_s, int N, int B, int lg_ncc, const float* W, int H_r, int RPW,
+                  int G, const unsigned short* V, int64_t ldV, unsigned short* O,
+                  int64_t ldO, int RG, const Batch& bt, int R) {
+#define MF_CASE(NCH_)                                                                            \
+  case NCH_:                                                                                     \
+    if (kGeneral || bt.cu_rows)                                                                  \
+      hipLaunchKernelGGL((k_retrieve_pair<kBF16, NCH_, NPAIR, true>), grid, dim3(kThreads), 0, st, \
+                         row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_retrieve_pair<kBF16, NCH_, NPAIR, false>), grid, dim3(kThreads), 0, st, \
+                         row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
+    break;
+  switch (NCH) {
+    MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5)
+    default: return mf::fail(MF_ERR_UNSUPPORTED, "k_retrieve_pair: H_s out of range");
+  }
+#undef MF_CASE
+  return mf::hip_check(hipGetLastError(), "k_retrieve_pair launch");
+}
+
+// The matrix-core kernel for block size B: pair stages for B >= 32.
+template <bool kBF16, int NPAIR, bool kGeneral = false>
+int launch_mfma_any(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
+                    const int32_t* col_idx, const unsigned short* vals, int64_t nnzb,
+                    int H_s, int N, int B, int lg_ncc, const float* W, int H_r, int RPW,
+                    int G, const unsigned short* V, int64_t ldV, unsigned short* O,
+                    int64_t ldO, int RG, const Batch& bt, int R) {
+  // 41-48 sender heads (NCH = 6) keep the first form: with pair stages its
+  // register set no longer fits without spilling
+  if (B >= 32 && NCH <= 5)
+    return launch_pair_p<kBF16, NPAIR, kGeneral>(NCH, grid, st, row_ptr, col_idx, vals, nnzb, H_s, N, B,
+                                                 lg_ncc, W, H_r, RPW, G, V, ldV, O, ldO, RG, bt, R);
+  return launch_mfma_p<kBF16, NPAIR, kGeneral>(NCH, grid, st, row_ptr, col_idx, vals, nnzb, H_s, N, B,
+                                               lg_ncc, W, H_r, RPW, G, V, ldV, O, ldO, RG, bt, R);
+}
+
 }  // namespace
 
 namespace mf {
@@ -907,10 +1371,10 @@ int retrieve_impl(const int32_t* row_ptr, const int32_t* col_idx, const void* va
     auto Op = reinterpret_cast<unsigned short*>(O);
     const bool bf = dt == MF_BF16;
     if (RPW > 2)
-      return bf ? launch_mfma_p<true, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
-                : launch_mfma_p<false, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
-    return bf ? launch_mfma_p<true, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
-              : launch_mfma_p<false, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
+      return bf ? launch_mfma_any<true, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
+                : launch_mfma_any<false, 2>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
+    return bf ? launch_mfma_any<true, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R)
+              : launch_mfma_any<false, 1>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op, ldO, RG, bt, R);
   }
   if (dt == MF_F32)
     return launch_simple<mfd::TF32>(B, d, row_ptr, col_idx, vals, nnzb, H_s, N, W, H_r, V, H_kv, ldV, O, ldO, bt, R, st);
@@ -966,10 +1430,10 @@ int launch_retrieve_multi(const int32_t* row_ptr, const int32_t* col_idx, const 
   auto O0 = reinterpret_cast<unsigned short*>(r0.O);
   const bool bf = dt == MF_BF16;
   if (max_rpw > 2)
-    return bf ? launch_mfma_p<true, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
-              : launch_mfma_p<false, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
-  return bf ? launch_mfma_p<true, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
-            : launch_mfma_p<false, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
+    return bf ? launch_mfma_any<true, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
+              : launch_mfma_any<false, 2, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
+  return bf ? launch_mfma_any<true, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R)
+            : launch_mfma_any<false, 1, true>(NCH, grid, st, row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, r0.W, r0.H_r, r0.RPW, r0.G, V0, r0.ldV, O0, r0.ldO, RG, bt, R);
 }
 
 int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_t* cu_rows,

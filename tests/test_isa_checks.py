@@ -113,9 +113,16 @@ def retrieve_asm(tmp_path_factory):
     return str(out)
 
 
-@pytest.mark.parametrize("tag", KERNELS)
+# pair-stage kernels (B >= 32, up to 40 sender heads): bf16/fp16, 1 or 2
+# receiver pairs, the head-mix plans, one sequence or a packed batch
+PAIR_KERNELS = [k + v for k in ("ILb1ELi5ELi2E", "ILb1ELi3ELi1E", "ILb1ELi4ELi2E", "ILb0ELi4ELi2E",
+                                "ILb0ELi5ELi1E", "ILb1ELi1ELi1E", "ILb1ELi2ELi2E") for v in ("Lb0E", "Lb1E")]
+
+
+@pytest.mark.parametrize("tag", ["k_retrieve_mfma" + t for t in KERNELS] +
+                         ["k_retrieve_pair" + t for t in PAIR_KERNELS])
 def test_retrieve_kernels_have_no_hazards(retrieve_asm, tag):
-    res = isa_check.check_asm(retrieve_asm, pattern="k_retrieve_mfma" + tag)
+    res = isa_check.check_asm(retrieve_asm, pattern=tag)
     assert len(res) == 1, tag
     (name, r), = res.items()
     assert r["scratch"] == 0, name
