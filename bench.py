@@ -311,7 +311,9 @@ def single_layer_leg(dev, name, reps):
     H_s = 32, H_r = 32, H_kv = 8, fp16, p = 0.9).  The layer is generated and
     compressed (untimed), its dense map freed, and the retrieval timed with HIP
     events `reps` times, each after a 512 MB scrub; median and spread, and the
-    roofline from the same algorithmic bytes as the headline."""
+    roofline from the same algorithmic bytes as the headline.  Where the
+    library splits long block rows (near-dense maps), the retrieval gets the
+    workspace for it, and the same layer with rows kept whole is timed beside."""
     import torch
     import cross_model_sparse_amd as mf
     import synth
@@ -330,17 +332,25 @@ def single_layer_leg(dev, name, reps):
     O = torch.empty(N, w.H_r, w.d, dtype=V.dtype, device=dev)
     buf = torch.zeros(512 << 18, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O)
-    ts = []
-    for _ in range(reps):
-        scrub(buf)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O)
-        b.record(stream)
-        b.synchronize()
-        ts.append(a.elapsed_time(b) * 1e3)
-    st = launch_stats(ts)
+    # a workspace that lets the library split long block rows (0 bytes when
+    # splitting does not apply to this layer)
+    ws_bytes = mf.retrieve_split_workspace_bytes(nnzb, V.dtype, w.H_s, N, B, w.H_r, w.H_kv, w.d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def timed(workspace):
+        mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O, workspace=workspace)
+        ts = []
+        for _ in range(reps):
+            scrub(buf)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            mf.retrieve_fused(rp, ci, vals, nnzb, W, V, N, B, out=O, workspace=workspace)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return launch_stats(ts)
+    st = timed(ws)
+    st_whole = timed(None) if ws is not None else None
     alg = (nnzb * w.H_s * B * B * e + N * w.H_kv * w.d * e + N * w.H_r * w.d * e
            + 4 * (T + 1 + nnzb) + 4 * w.H_r * w.H_s)
     flops = 2.0 * nnzb * w.H_r * B * B * (w.H_s + w.d)
@@ -353,6 +363,8 @@ def single_layer_leg(dev, name, reps):
            "kept_per_row": {"min": int(rows.min()), "max": int(rows.max()),
                             "mean": float(rows.mean())},
            "retrieve_us": st,
+           "split_rows": ws is not None,
+           "retrieve_us_rows_whole": st_whole,
            "query_tokens_per_s": N / t,
            "roofline": {"bound": "hbm", "bytes_per_launch": alg, "achieved": alg / t / 1e9,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": alg / t / 1e9 / HBM_PEAK_GBS,

@@ -6,7 +6,8 @@ binding over torch device tensors.
 """
 from .mapflow import (  # noqa: F401
     MapflowError, CapacityError, abi_version, block_mass, block_mass_ws_bytes, topp_select_bsr,
-    retrieve_fused, retrieve_fused_multi, retrieve_fused_varlen, retrieve_kernel, compress, topp_workspace_bytes, retrieve_workspace_bytes, load, lib_path, EXPORTED,
+    topp_select_bsr_noalloc,
+    retrieve_fused, retrieve_fused_multi, retrieve_fused_varlen, retrieve_kernel, compress, topp_workspace_bytes, retrieve_workspace_bytes, retrieve_split_workspace_bytes, load, lib_path, EXPORTED,
     row_lse, block_mass_qk, block_mass_qk_workspace_bytes, lse_block_mass_qk,
     lse_block_mass_qk_workspace_bytes, topp_select_bsr_qk, compress_qk,
     BlockManager, prefix_hashes, pool_store,

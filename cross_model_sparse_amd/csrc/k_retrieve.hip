@@ -746,6 +746,74 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 // last chunk has passed a barrier: it is issued between the A.V MFMAs of
 // phase 2P-3 and waited for at the end of phase 2P-2.
 
+// Split rows.  When a few long block rows would set the time of a launch (the
+// rows of a near-dense map run from 1 to T kept blocks), every row with more
+// than P kept blocks is cut into ceil(cnt / P) parts of balanced length.  The
+// work items are then the rows from the last to the first, each row's parts in
+// order; a part writes its fp32 partial output to the workspace, and
+// k_split_combine adds a row's partials in part order, so the output is the
+// same bit for bit on every run.  Rows of at most P blocks write O directly.
+struct Split {
+  float* part;            // [item][slice][16 rows][H_r][128] fp32 partials
+  int32_t* first_item;    // [T] item index of part 0 of each split row
+  int P;                  // longest part, in kept blocks
+};
+__device__ __forceinline__ int split_parts(int64_t cnt, int P) {
+  return cnt > P ? (int)((cnt + P - 1) / P) : 1;
+}
+// Item j of the split list -> block row I, part index, part count; false when
+// j is past the last item.  All 512 threads of the workgroup take part; `buf`
+// is LDS for 8 + 4 ints.
+__device__ bool split_item(const int32_t* __restrict__ row_ptr, int64_t nnzb, int T, int P, int j,
+                           int* buf, int& I, int& part, int& parts) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per = (T + kThreads - 1) / kThreads;  // item-order rows per thread
+  const int i0 = tid * per;
+  auto row_cnt = [&](int i) -> int64_t {          // kept blocks of the i-th row in item order
+    const int r = T - 1 - i;
+    int64_t kb = row_ptr[r], ke = row_ptr[r + 1];
+    kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
+    ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
+    return ke - kb;
+  };
+  int mine = 0;
+  for (int i = i0; i < i0 + per && i < T; ++i) mine += split_parts(row_cnt(i), P);
+  int incl = mine;                                // inclusive scan within the wavefront
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) buf[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = buf[w];
+    base += w < wave ? v : 0;
+    total += v;
+  }
+  const int excl = base + incl - mine;
+  if (j >= excl && j < excl + mine) {             // this thread's rows hold item j
+    int k = excl;
+    for (int i = i0; i < i0 + per && i < T; ++i) {
+      const int np = split_parts(row_cnt(i), P);
+      if (j < k + np) {
+        buf[kWaves] = T - 1 - i;
+        buf[kWaves + 1] = j - k;
+        buf[kWaves + 2] = np;
+        break;
+      }
+      k += np;
+    }
+  }
+  __syncthreads();
+  I = buf[kWaves];
+  part = buf[kWaves + 1];
+  parts = buf[kWaves + 2];
+  __syncthreads();                                // buf is reused by the caller
+  return j < total;
+}
+
 // 8 bytes per lane from memory into a register pair: wave-uniform base and a
 // 32-bit per-lane byte offset, or a per-lane address.  The registers receive
 // the data asynchronously; they are read only after wait_vm_regs() has
@@ -768,7 +836,7 @@ __device__ __forceinline__ void wait_vm_regs(u32x2 (&x)[8]) {
                : "n"(N) : "memory");
 }
 
-template <bool kBF16, int NCH, int NPAIR, bool kVar>
+template <bool kBF16, int NCH, int NPAIR, bool kVar, bool kSplit = false>
 __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const unsigned short* __restrict__ vals, int64_t nnzb, int H_s, int N, int B,
@@ -776,7 +844,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     const unsigned short* __restrict__ V, int64_t ldV,
     unsigned short* __restrict__ O, int64_t ldO, int RG, Batch bt,
     const int32_t* __restrict__ cu_rows, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ block_table, int R) {
+    const int32_t* __restrict__ block_table, int R, Split sp) {
+  static_assert(!(kSplit && kVar), "split rows: one sequence, one receiver");
   using Plan = HmPlan<kBF16, NCH>;
   constexpr int NBOP = Plan::NBOP;
   constexpr int NPL = kBF16 ? 2 : 1;               // mixed-map planes (hi, lo)
@@ -810,7 +879,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     }
   }
   int Ig, sub;
-  if (!item_of(bid, subs, R, RG, &Ig, &sub)) return;
+  int part = 0, parts = 1, item = 0;             // split rows: this item's part of its row
+  if constexpr (kSplit) {
+    // items dealt to the XCDs in turn, the slices of one item on one XCD
+    const int local = bid >> 3;
+    sub = local % subs;
+    item = (local / subs) * 8 + (bid & 7);
+    if (!split_item(row_ptr, nnzb, R, sp.P, item, reinterpret_cast<int*>(smem), Ig, part, parts))
+      return;
+  } else {
+    if (!item_of(bid, subs, R, RG, &Ig, &sub)) return;
+  }
   RowView rv;
   if (!row_view<kVar>(bt, cu_rows, cu_seqlens, Ig, N, B, rv)) return;
   const int I = rv.I;
@@ -866,12 +945,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   int64_t kb = row_ptr[Ig], ke = row_ptr[Ig + 1];
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
+  if constexpr (kSplit) {
+    if (parts > 1) {                             // this part's balanced share of the row
+      const int64_t len = (ke - kb + parts - 1) / parts;
+      const int64_t k0 = kb + part * len;
+      ke = k0 + len < ke ? k0 + len : ke;
+      kb = k0 < ke ? k0 : ke;
+      if (part == 0 && sub == 0 && threadIdx.x == 0) sp.first_item[Ig] = item;
+    }
+  }
   const int lg_npb = lg_ncc - 1;                 // pairs per block: B / 32
   const int npb_mask = (1 << lg_npb) - 1;
   const int cnt = (int)(ke - kb);
   const int n_chunks = cnt << lg_ncc;
   const int64_t tile = (int64_t)B * B;
-  const int rot = cnt > 0 ? cnt - 1 - I % cnt : 0;
+  const int rot = (cnt > 0 && parts == 1) ? cnt - 1 - I % cnt : 0;
   auto block_of = [&](int x) -> int64_t {        // kept block of chunk x (clamped)
     x = x < n_chunks ? x : n_chunks - 1;
     const int t = (x >> lg_ncc) + rot;
@@ -1122,6 +1210,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   wait_vm<0>();
   lds_barrier();
 
+  // ---- a part of a split row: fp32 partials, 16 bytes (4 head-dim columns) per lane
+  if constexpr (kSplit) {
+    if (parts > 1) {
+      float* pp = sp.part + (int64_t)(item * subs + sub) * kRows * H_r * kD;
+#pragma unroll
+      for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (2 * p + (m >> 4) < RPW)
+            *reinterpret_cast<f32x4*>(pp + ((m & 15) * H_r + rbeg + 2 * p + (m >> 4)) * kD + 4 * am) =
+                f32x4{acc[p][0][e], acc[p][1][e], acc[p][2][e], acc[p][3][e]};
+        }
+      return;
+    }
+  }
+
   // ---- store through LDS (as in k_retrieve_mfma) ------------------------------
   unsigned short* ot = reinterpret_cast<unsigned short*>(smem + wave * kOutSlot);
 #pragma unroll
@@ -1146,6 +1251,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
       if (2 * p + rp < RPW && grow < N)
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(O + grow * ldO + (int64_t)(rbeg + 2 * p + rp) * kD + d8));
     }
+  }
+}
+
+// O rows of the split block rows: the sum of the row's part partials in part
+// order, rounded once to the output type.  One workgroup per (block row,
+// 16-row slice); rows kept whole return at once.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void k_split_combine(
+    const int32_t* __restrict__ row_ptr, int64_t nnzb, int T, int N, int B, int H_r,
+    unsigned short* __restrict__ O, int64_t ldO, Split sp) {
+  const int I = blockIdx.x, sub = blockIdx.y;
+  const int subs = B / kRows;
+  int64_t kb = row_ptr[I], ke = row_ptr[I + 1];
+  kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
+  ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
+  const int parts = split_parts(ke - kb, sp.P);
+  if (parts == 1) return;
+  const int j0 = sp.first_item[I];
+  const int64_t slot = (int64_t)kRows * H_r * kD;     // floats per (item, slice)
+  const int n4 = (int)(slot / 4);
+  for (int e4 = threadIdx.x; e4 < n4; e4 += 256) {
+    const int e = 4 * e4;
+    const int row = e / (H_r * kD);
+    const int64_t grow = (int64_t)I * B + sub * kRows + row;
+    if (grow >= N) continue;
+    f32x4 s = *reinterpret_cast<const f32x4*>(sp.part + (int64_t)(j0 * subs + sub) * slot + e);
+    for (int p = 1; p < parts; ++p) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sp.part + (int64_t)((j0 + p) * subs + sub) * slot + e);
+      s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+    }
+    const int rc = e - row * H_r * kD;            // receiver * 128 + column
+    unsigned short h[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) h[t] = kBF16 ? bf16_bits(s[t]) : f32_to_f16(s[t]);
+    *reinterpret_cast<u32x2*>(O + grow * ldO + rc) =
+        u32x2{(unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16)};
   }
 }
 
@@ -1298,11 +1439,11 @@ int launch_pair_p(int NCH, dim3 grid, hipStream_t st, const int32_t* row_ptr,
     if (kGeneral || bt.cu_rows)                                                                  \
       hipLaunchKernelGGL((k_retrieve_pair<kBF16, NCH_, NPAIR, true>), grid, dim3(kThreads), 0, st, \
                          row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
-                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R, Split{}); \
     else                                                                                         \
       hipLaunchKernelGGL((k_retrieve_pair<kBF16, NCH_, NPAIR, false>), grid, dim3(kThreads), 0, st, \
                          row_ptr, col_idx, vals, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G,        \
-                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R);   \
+                         V, ldV, O, ldO, RG, bt, bt.cu_rows, bt.cu_seqlens, bt.block_table, R, Split{}); \
     break;
   switch (NCH) {
     MF_CASE(1) MF_CASE(2) MF_CASE(3) MF_CASE(4) MF_CASE(5)
@@ -1350,14 +1491,108 @@ bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const 
 size_t retrieve_workspace_bytes(int, int, int, int, int) { return 0; }
 
 namespace {
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+int split_part_len(int64_t nnzb, int B) {
+  const int64_t work = nnzb * (B / kRows);        // (kept block, 16-row slice) units
+  const int64_t cus = device_cus();
+  const int64_t P = (work + cus - 1) / cus;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(P, 1 << 20));
+}
+
+// Splitting pays when the average row is longer than half the per-CU share P:
+// then there are too few items per CU for the longest rows to even out.
+bool split_applies(int dt, int H_s, int N, int B, int H_r, int H_kv, int d, int64_t nnzb) {
+  if (dt == MF_F32 || d != kD || B < 32 || (H_s + 7) / 8 > 5 || H_r % 8 != 0 || H_r > kMaxRecv) return false;
+  const int G = H_r / H_kv, RPW = H_r / 8;
+  if (G % RPW != 0 || nnzb <= 0) return false;
+  const int T = blocks_of(N, B);
+  return 2 * nnzb > (int64_t)split_part_len(nnzb, B) * T;
+}
+
+size_t split_workspace_bytes(int dt, int H_s, int N, int B, int H_r, int H_kv, int d, int64_t nnzb) {
+  if (!split_applies(dt, H_s, N, B, H_r, H_kv, d, nnzb)) return 0;
+  const int T = blocks_of(N, B);
+  const int64_t items = T + nnzb / split_part_len(nnzb, B);
+  return align256((size_t)items * (B / kRows) * kRows * H_r * kD * sizeof(float)) +
+         align256((size_t)T * sizeof(int32_t));
+}
+
+namespace {
 
 // R block rows (all sequences of bt); N is the single sequence's length when
 // bt.cu_rows is null.
+// Split-row launch (one sequence, one receiver, pair kernel): the retrieval
+// over the split work list, then the partial sums of the split rows.
+int launch_split(const int32_t* row_ptr, const int32_t* col_idx, const void* vals, int64_t nnzb,
+                 int dt, int H_s, int N, int B, const float* W, int H_r, const void* V, int H_kv,
+                 int64_t ldV, void* O, int64_t ldO, void* workspace, hipStream_t st) {
+  const int T = blocks_of(N, B);
+  const int subs = B / kRows;
+  const int P = split_part_len(nnzb, B);
+  const int64_t items = T + nnzb / P;
+  const size_t part_bytes = align256((size_t)items * subs * kRows * H_r * kD * sizeof(float));
+  Split sp{reinterpret_cast<float*>(workspace),
+           reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part_bytes), P};
+  const Batch bt{nullptr, nullptr, nullptr, nnzb, 1, 1, {}};
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8 * subs));
+  const int NCH = (H_s + 7) / 8;
+  const int RPW = H_r / 8, G = H_r / H_kv;
+  const int lg_ncc = B == 32 ? 1 : B == 64 ? 2 : 3;
+  auto vp = reinterpret_cast<const unsigned short*>(vals);
+  auto Vs = reinterpret_cast<const unsigned short*>(V);
+  auto Op = reinterpret_cast<unsigned short*>(O);
+  const bool bf = dt == MF_BF16;
+#define MF_SPLIT(BF_, NP_, NCH_)                                                                   \
+  hipLaunchKernelGGL((k_retrieve_pair<BF_, NCH_, NP_, false, true>), grid, dim3(kThreads), 0, st,  \
+                     row_ptr, col_idx, vp, nnzb, H_s, N, B, lg_ncc, W, H_r, RPW, G, Vs, ldV, Op,  \
+                     ldO, 1, bt, nullptr, nullptr, nullptr, T, sp)
+#define MF_SPLIT_NCH(BF_, NP_)                                                                    \
+  switch (NCH) {                                                                                \
+    case 1: MF_SPLIT(BF_, NP_, 1); break;                                                       \
+    case 2: MF_SPLIT(BF_, NP_, 2); break;                                                       \
+    case 3: MF_SPLIT(BF_, NP_, 3); break;                                                       \
+    case 4: MF_SPLIT(BF_, NP_, 4); break;                                                       \
+    default: MF_SPLIT(BF_, NP_, 5); break;                                                      \
+  }
+  if (bf) {
+    if (RPW > 2) { MF_SPLIT_NCH(true, 2) } else { MF_SPLIT_NCH(true, 1) }
+  } else {
+    if (RPW > 2) { MF_SPLIT_NCH(false, 2) } else { MF_SPLIT_NCH(false, 1) }
+  }
+#undef MF_SPLIT_NCH
+#undef MF_SPLIT
+  int r = mf::hip_check(hipGetLastError(), "k_retrieve_pair (split rows) launch");
+  if (r != MF_OK) return r;
+  if (bf)
+    hipLaunchKernelGGL(k_split_combine<true>, dim3(T, subs), dim3(256), 0, st, row_ptr, nnzb, T, N, B,
+                       H_r, Op, ldO, sp);
+  else
+    hipLaunchKernelGGL(k_split_combine<false>, dim3(T, subs), dim3(256), 0, st, row_ptr, nnzb, T, N, B,
+                       H_r, Op, ldO, sp);
+  return mf::hip_check(hipGetLastError(), "k_split_combine launch");
+}
+
 int retrieve_impl(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,
                   int64_t nnzb, int dt, int H_s, int N, int B, const float* W, int H_r,
                   const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
-                  const Batch& bt, int R, hipStream_t st) {
+                  const Batch& bt, int R, hipStream_t st, void* workspace = nullptr,
+                  size_t workspace_bytes = 0) {
   if (R <= 0) return MF_OK;
+  if (bt.cu_rows == nullptr && bt.n_recv == 1 && workspace != nullptr &&
+      retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO) &&
+      split_applies(dt, H_s, N, B, H_r, H_kv, d, nnzb) &&
+      workspace_bytes >= split_workspace_bytes(dt, H_s, N, B, H_r, H_kv, d, nnzb))
+    return launch_split(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W, H_r, V, H_kv, ldV, O, ldO,
+                        workspace, st);
   if (retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO)) {
     const int RG = std::max(1, R / 16);
     const int groups = (R + RG - 1) / RG;
@@ -1388,11 +1623,11 @@ int retrieve_impl(const int32_t* row_ptr, const int32_t* col_idx, const void* va
 int launch_retrieve(const int32_t* row_ptr, const int32_t* col_idx,
                     const void* vals, int64_t nnzb, int dt, int H_s, int N,
                     int B, const float* W, int H_r, const void* V, int H_kv,
-                    int d, int64_t ldV, void* O, int64_t ldO, void*, size_t,
-                    hipStream_t st) {
+                    int d, int64_t ldV, void* O, int64_t ldO, void* workspace,
+                    size_t workspace_bytes, hipStream_t st) {
   const Batch bt{nullptr, nullptr, nullptr, nnzb, 1, 1, {}};
   return retrieve_impl(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W, H_r, V, H_kv, d, ldV,
-                       O, ldO, bt, blocks_of(N, B), st);
+                       O, ldO, bt, blocks_of(N, B), st, workspace, workspace_bytes);
 }
 
 int launch_retrieve_multi(const int32_t* row_ptr, const int32_t* col_idx, const void* vals,

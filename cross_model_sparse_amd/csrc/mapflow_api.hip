@@ -340,6 +340,14 @@ size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype) {
   return mf::retrieve_workspace_bytes(N, B, H_kv, d, dtype);
 }
 
+size_t mf_retrieve_split_workspace_bytes(int64_t nnzb, int dtype, int H_s, int N, int B, int H_r,
+                                         int H_kv, int d) {
+  if (nnzb <= 0 || N < 1 || !valid_block(B) || !valid_dtype(dtype) || H_s < 1 || H_s > 64 ||
+      H_r < 1 || H_r > 64 || H_kv < 1 || H_r % H_kv != 0)
+    return 0;
+  return mf::split_workspace_bytes(dtype, H_s, N, B, H_r, H_kv, d, nnzb);
+}
+
 // Shape and stride checks shared by mf_retrieve_fused and mf_retrieve_kernel.
 static int check_retrieve_shape(const char* fn, int dtype, int H_s, int N, int B, int H_r,
                                 int H_kv, int d, int64_t ldV, int64_t ldO) {

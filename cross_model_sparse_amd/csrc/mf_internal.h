@@ -80,6 +80,10 @@ int launch_retrieve_varlen(int S, int R, const int32_t* cu_seqlens, const int32_
                            const void* V, int H_kv, int d, int64_t ldV, void* O, int64_t ldO,
                            hipStream_t st);
 size_t retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dt);
+// Workspace that lets launch_retrieve split long block rows (0 when splitting
+// does not apply to these shapes); split_part_len is the longest part.
+size_t split_workspace_bytes(int dt, int H_s, int N, int B, int H_r, int H_kv, int d, int64_t nnzb);
+int split_part_len(int64_t nnzb, int B);
 // True when launch_retrieve runs the matrix-core kernel for these arguments.
 bool retrieve_uses_mfma(int dt, int H_s, int B, int H_r, int H_kv, int d, const void* vals,
                         const void* V, int64_t ldV, const void* O, int64_t ldO);

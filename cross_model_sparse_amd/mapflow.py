@@ -27,7 +27,8 @@ EXPORTED = ("mf_abi_version", "mf_status_string", "mf_last_error", "mf_block_mas
             "mf_topp_workspace_bytes", "mf_topp_select_bsr", "mf_topp_select_bsr_noalloc", "mf_row_lse",
             "mf_block_mass_qk_workspace_bytes", "mf_block_mass_qk",
             "mf_lse_block_mass_qk_workspace_bytes", "mf_lse_block_mass_qk", "mf_topp_select_bsr_qk",
-            "mf_retrieve_workspace_bytes", "mf_retrieve_kernel", "mf_retrieve_fused",
+            "mf_retrieve_workspace_bytes", "mf_retrieve_split_workspace_bytes", "mf_retrieve_kernel",
+            "mf_retrieve_fused",
             "mf_retrieve_fused_multi", "mf_retrieve_fused_varlen", "mf_prefix_hashes",
             "mf_bm_create", "mf_bm_destroy", "mf_bm_lookup", "mf_bm_release", "mf_bm_insert",
             "mf_bm_stats", "mf_pool_store")
@@ -99,6 +100,8 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(c_i64), c_vp, c_sz, c_vp]
     L.mf_retrieve_workspace_bytes.restype = c_sz
     L.mf_retrieve_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int]
+    L.mf_retrieve_split_workspace_bytes.restype = c_sz
+    L.mf_retrieve_split_workspace_bytes.argtypes = [c_i64, c_int, c_int, c_int, c_int, c_int, c_int, c_int]
     L.mf_retrieve_kernel.restype = c_int
     L.mf_retrieve_kernel.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
                                      c_vp, c_i64, c_vp, c_i64]
@@ -207,6 +210,13 @@ def topp_workspace_bytes(N: int, B: int) -> int:
 
 def retrieve_workspace_bytes(N: int, B: int, H_kv: int, d: int, dtype: torch.dtype) -> int:
     return int(load().mf_retrieve_workspace_bytes(N, B, H_kv, d, _DTYPE_CODE[dtype]))
+
+
+def retrieve_split_workspace_bytes(nnzb: int, dtype: torch.dtype, H_s: int, N: int, B: int,
+                                   H_r: int, H_kv: int, d: int) -> int:
+    """Workspace bytes that let retrieve_fused split long block rows (0: no split)."""
+    return int(load().mf_retrieve_split_workspace_bytes(int(nnzb), _DTYPE_CODE[dtype], H_s, N, B,
+                                                        H_r, H_kv, d))
 
 
 def block_mass_ws_bytes(H_s: int, N: int, B: int) -> int:

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MF_ABI_VERSION 6
+#define MF_ABI_VERSION 7
 
 typedef enum {
   MF_OK = 0,
@@ -266,6 +266,25 @@ int mf_topp_select_bsr_qk(const float* mass, const void* Q, const void* K,
 size_t mf_retrieve_workspace_bytes(int N, int B, int H_kv, int d, int dtype);
 
 /*
+ * Workspace bytes that let mf_retrieve_fused split long block rows (article,
+ * third section, second component: different layers and positions keep
+ * different numbers of blocks, so a few long rows can set the time of a
+ * launch).  With a workspace of at least this size, a launch whose average
+ * row is longer than half of one CU's share of the work cuts every row of
+ * more than P = ceil(nnzb * B/16 / CUs) kept blocks into parts of at most P
+ * blocks, runs the parts as separate work items (rows from the last to the
+ * first) and adds each split row's fp32 partial outputs in part order in a
+ * second kernel, so the output is bitwise the same on every run.  It is
+ * still the sum of the same products, not bitwise the unsplit output.  Returns
+ * 0 when splitting does not apply to these shapes (they take the matrix-core
+ * kernel with pair stages only: fp16/bf16, d = 128, B >= 32, H_s <= 40, H_r in
+ * {8,16,24,32}), for nnzb <= 0 or for invalid arguments.  The size grows
+ * with nnzb: (T + nnzb/P) items x B rows x H_r x 128 fp32, plus 4*T bytes.
+ */
+size_t mf_retrieve_split_workspace_bytes(int64_t nnzb, int dtype, int H_s, int N, int B, int H_r,
+                                         int H_kv, int d);
+
+/*
  * Which retrieval kernel mf_retrieve_fused runs for these arguments (host
  * only, no GPU work; the three pointers are inspected for alignment only and
  * may be any address with the alignment the real buffers will have).
@@ -304,7 +323,10 @@ int mf_retrieve_kernel(int dtype, int H_s, int N, int B, int H_r, int H_kv, int 
  *            tensor): V[n][g][e] at V[n*ldV + g*d + e], n < N.
  *  O         device, O[n][r][e] at O[n*ldO + r*d + e], ldO >= H_r*d.
  *  workspace device scratch of >= mf_retrieve_workspace_bytes(...) bytes
- *            (NULL when that is 0, as it is for every current kernel).
+ *            (NULL when that is 0, as it is for every current kernel).  A
+ *            workspace of >= mf_retrieve_split_workspace_bytes(...) bytes
+ *            turns on the splitting of long block rows described there; its
+ *            contents need no initialisation.
  *  Precision: MF_F32 runs in fp32 throughout.  MF_BF16: the head mix runs on
  *  bf16 matrix cores with W split into two bf16 halves (W enters exactly) and
  *  fp32 accumulation; the fp32 mixed map is split the same way into hi + lo

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert mf.abi_version() == 6
+    assert mf.abi_version() == 7
     for st in range(5):
         assert L.mf_status_string(st)
     assert b"unknown" in L.mf_status_string(99)
