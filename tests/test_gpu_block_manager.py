@@ -1,5 +1,6 @@
 """GPU side of the Block Manager: tile copies into the pool, and a cached
-prefix reused end to end.
+prefix reused end to end, also against the oracle's retrieval through the
+same pool pages.
 
 A causal map's rows below position n depend on tokens 0..n-1 only, so the map
 of a sequence's first n tokens is exactly the top-left n x n corner of the
@@ -18,7 +19,9 @@ import pytest
 import torch
 
 import cross_model_sparse_amd as mf
+import oracle
 import synth
+from tests._compare import check_output
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +89,19 @@ def test_cached_prefix_serves_the_longer_sequence(recipe, N, n_pre):
     O_fresh = mf.retrieve_fused(rp, ci, vals, nz, W, V, N, B)
     torch.cuda.synchronize()
     assert torch.equal(O_cache, O_fresh)
+    # the cached path against the oracle: its own compression of the host copy
+    # of the map, its tiles placed in a host pool at the manager's pages, and
+    # its packed-batch retrieval through the same block table
+    A_h = A.float().cpu().numpy()
+    _, _, rp_o, ci_o, vals_o = oracle.compress(A_h, B, p)
+    assert np.array_equal(rp_o, rp_h) and np.array_equal(ci_o, ci_h), "selection differs from the oracle"
+    tab = table.cpu().numpy().astype(np.int64)
+    pool_o = np.zeros((n_pages,) + vals_o.shape[1:], dtype=vals_o.dtype)
+    pool_o[tab] = vals_o
+    O_ref = oracle.retrieve_varlen([0, N], [0, w.T], rp_o, ci_o, pool_o, L["W"].numpy(),
+                                   L["V"].float().numpy(), B, block_table=tab)
+    rel = check_output(O_cache.float().cpu().numpy(), O_ref, w.dtype)
+    say(f"[bm] cached path vs oracle: max err/max = {rel:.3e}")
     s = bm.stats()
     assert s["hits"] == k_rows and s["held_rows"] == k_rows
     bm.release(0, tokens, k_rows)

@@ -291,6 +291,32 @@ def test_repeat_runs_are_bitwise_identical(gpu):
             assert a == b
 
 
+def test_selection_at_max_block_rows_kept_sets(gpu):
+    """T = 4096 block rows (B = 16, one sender head): the kept columns of
+    sampled rows equal the oracle's Top-p sets, ties aside.  The masses are
+    random; the map only supplies tiles (never compared), so it is left
+    uninitialised."""
+    T, B = 4096, 16
+    N = T * B
+    g = torch.Generator().manual_seed(78)
+    mass = torch.tril(torch.rand(T, T, generator=g) ** 6).contiguous()
+    A = torch.empty(1, N, N, dtype=torch.float16, device=gpu)       # 8.6 GB, never read back
+    rp, ci, vals, nnzb = mf.topp_select_bsr(mass.to(gpu), A, B, 0.9)
+    g_rp = host(rp).astype(np.int64)
+    g_ci = host(ci[:nnzb]).astype(np.int64)
+    m32 = mass.numpy().astype(np.float64)
+    ties = 0
+    rows = [0, 1, 2, 100, 1023, 1024, 2047, 3000] + list(range(4088, 4096))
+    for I in rows:
+        kept_ref = oracle.topp_row(oracle.decision_masses(m32[I, : I + 1]), 0.9)
+        kept_gpu = g_ci[g_rp[I]:g_rp[I + 1]]
+        assert np.all(np.diff(kept_gpu) > 0) and kept_gpu[0] >= 0 and kept_gpu[-1] <= I
+        ties += selection_ok(m32[I, : I + 1], kept_ref, kept_gpu, 0.9) == "tie"
+    say(f"[T=4096] nnzb={nnzb} rows checked={len(rows)} ties={ties}")
+    assert ties <= 1
+    del A, vals
+
+
 def test_selection_at_max_block_rows(gpu):
     """T = 4096 block rows: selection counts equal the oracle's on sampled rows.
     Capacity 0, so the map itself is never read."""
@@ -329,8 +355,9 @@ def _sample_rows(T, extra=6, seed=0):
 
 
 def test_full_pair14b8b_bf16_layer(gpu):
+    """The headline layer at full size, every block row checked."""
     w = synth.workload("pair14b8b-bf16")
-    nnzb, mass, rp, O = run_end_to_end(w, gpu, rows=_sample_rows(w.T), layer=3)
+    nnzb, mass, rp, O = run_end_to_end(w, gpu, layer=3)
     dens = nnzb / (w.T * (w.T + 1) / 2)
     assert 0.05 <= dens <= 0.25, dens
     m = host(mass)
@@ -347,7 +374,9 @@ def test_full_pair8b3b_f16_every_row(gpu):
 
 def test_full_long32k_f16(gpu):
     w = synth.workload("long32k-f16")
-    nnzb, *_ = run_end_to_end(w, gpu, rows=_sample_rows(w.T, extra=3))
+    rows = _sample_rows(w.T, extra=30)
+    assert len(rows) >= 32
+    nnzb, *_ = run_end_to_end(w, gpu, rows=rows)
     dens = nnzb / (w.T * (w.T + 1) / 2)
     say(f"[long] density {dens:.3f}")
     assert 0.03 <= dens <= 0.2, dens
@@ -364,6 +393,20 @@ def test_full_varlen_sequences(gpu):
             w = w0.with_(N=n)
             run_end_to_end(w, gpu, rows=_sample_rows(w.T, extra=2, seed=i), p=p,
                            seed=5000 + lens.index(n))
+
+
+def test_full_long32k_past_2_31_elements(gpu):
+    """Long-context layer at p = 0.97: the compressed state passes 2^31
+    elements of vals (4096 blocks of 32 x 128 x 128), so block offsets in the
+    gather and the retrieval need 64 bits.  Sampled rows, the last ones
+    (whose blocks sit beyond 2^31 elements) among them, against the oracle."""
+    w = synth.workload("long32k-f16")
+    rows = sorted({0, 1, 128, 200} | set(range(w.T - 6, w.T)))
+    nnzb, mass, rp, O = run_end_to_end(w, gpu, rows=rows, p=0.97)
+    elems = nnzb * w.H_s * w.B * w.B
+    say(f"[long p=0.97] nnzb={nnzb}, vals elements {elems:.3e} (2^31 = {2**31:.3e})")
+    assert elems > 2 ** 31
+    assert int(host(rp)[w.T - 6]) * w.H_s * w.B * w.B > 2 ** 31   # the checked last rows lie past it
 
 
 @pytest.mark.parametrize("name,ov", [("pair14b8b-bf16", dict(N=1111)), ("tiny-f32", dict(N=250)),
