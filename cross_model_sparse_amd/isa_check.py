@@ -125,9 +125,42 @@ def _blocks(body):
     return order, blocks, succ
 
 
+_WAIT_VM = re.compile(r"s_waitcnt\s+.*vmcnt\((\d+)\)")
+
+
+def _decode(s):
+    """One instruction as the walk in _inflight needs it."""
+    parts = s.replace(",", " ").split()
+    op, ops = parts[0], parts[1:]
+    salu = None
+    if op.startswith("s_") and ops:
+        dst = ops[0]
+        if op == "s_mov_b64" and len(ops) > 1 and ops[1] in ("-1", "0"):
+            salu = ("set", dst, int(ops[1]))
+        elif op == "s_andn2_b64" and dst == "vcc" and len(ops) > 2 and ops[1] == "exec":
+            salu = ("andn2", ops[2])
+        else:
+            rng = set(range(*map(int, dst[2:-1].split(":")))) if dst.startswith("s[") else None
+            salu = ("kill", dst, rng)
+    m = _WAIT_VM.match(s)
+    if m:
+        return (salu, "wait", int(m.group(1)), None)
+    if VMEM.match(op):
+        is_load = "load" in op
+        dest = _vregs(ops[0]) if is_load and "lds" not in op else frozenset()
+        srcs = ops[1:] if is_load else ops
+        src = frozenset().union(*[_vregs(t) for t in srcs]) if srcs else frozenset()
+        return (salu, "vmem", dest, src)
+    if op.startswith("v_") or op.startswith("ds_"):
+        regs = frozenset().union(*[_vregs(t) for t in ops]) if ops else frozenset()
+        return (salu, "use", regs, None)
+    return (salu, None, None, None)
+
+
 def _inflight(body, max_states=64):
     """Lines touching the destination VGPRs of outstanding vector loads."""
     order, blocks, succ = _blocks(body)
+    code = {b: [(ln, s, _decode(s)) for ln, s in blocks[b]] for b in order}
     states = {b: set() for b in order}
     states["@0"].add(((), frozenset()))
     work = deque(["@0"])
@@ -136,44 +169,30 @@ def _inflight(body, max_states=64):
         b = work.popleft()
         for fifo0, consts0 in list(states[b]):
             fifo, consts = list(fifo0), dict(consts0)
-            for ln, s in blocks[b]:
-                parts = s.replace(",", " ").split()
-                op, ops = parts[0], parts[1:]
-                if op.startswith("s_") and ops:
-                    dst = ops[0]
-                    if op == "s_mov_b64" and len(ops) > 1 and ops[1] in ("-1", "0"):
-                        consts[dst] = int(ops[1])
-                    elif (op == "s_andn2_b64" and dst == "vcc" and len(ops) > 2
-                          and ops[1] == "exec" and ops[2] in consts):
-                        consts["vcc"] = 1 if consts[ops[2]] == 0 else 0
-                    else:
+            for ln, s, (salu, kind, x, y) in code[b]:
+                if salu is not None:
+                    if salu[0] == "set":
+                        consts[salu[1]] = salu[2]
+                    elif salu[0] == "andn2" and salu[1] in consts:
+                        consts["vcc"] = 1 if consts[salu[1]] == 0 else 0
+                    elif consts:
+                        dst, a = (salu[1], salu[2]) if salu[0] == "kill" else ("vcc", None)
                         for k in list(consts):
-                            if k == dst or dst == "vcc" and k == "vcc":
+                            if k == dst:
                                 consts.pop(k, None)
-                            elif dst.startswith("s[") and k.startswith("s["):
-                                a = set(range(*map(int, dst[2:-1].split(":"))))
-                                c = set(range(*map(int, k[2:-1].split(":"))))
-                                if a & c:
+                            elif a is not None and k.startswith("s["):
+                                if a & set(range(*map(int, k[2:-1].split(":")))):
                                     consts.pop(k, None)
-                m = re.match(r"s_waitcnt\s+.*vmcnt\((\d+)\)", s)
-                if m:
-                    keep = int(m.group(1))
-                    fifo = fifo[len(fifo) - keep:] if len(fifo) > keep else fifo
-                    continue
-                if VMEM.match(op):
-                    is_load = "load" in op
-                    dest = _vregs(ops[0]) if is_load and "lds" not in op else frozenset()
-                    srcs = ops[1:] if is_load else ops
-                    src = frozenset().union(*[_vregs(t) for t in srcs]) if srcs else frozenset()
+                if kind == "wait":
+                    fifo = fifo[len(fifo) - x:] if len(fifo) > x else fifo
+                elif kind == "vmem":
                     for d in fifo:
-                        if src & d or dest & d:
+                        if y & d or x & d:
                             bad.setdefault(ln, s)
-                    fifo.append(dest)
-                    continue
-                if op.startswith("v_") or op.startswith("ds_"):
-                    regs = frozenset().union(*[_vregs(t) for t in ops]) if ops else frozenset()
+                    fifo.append(x)
+                elif kind == "use" and fifo:
                     for d in fifo:
-                        if regs & d:
+                        if x & d:
                             bad.setdefault(ln, s)
             out = (tuple(fifo), frozenset(consts.items()))
             last = blocks[b][-1][1] if blocks[b] else ""
