@@ -72,7 +72,7 @@ def launch_stats(us):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_retrieve_mfma_pair14b8b_bf16_N8192_traffic.txt")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "k_retrieve_pair_pair14b8b_bf16_N8192_traffic.txt")
 KERNEL_SRC = os.path.join(HERE, "cross_model_sparse_amd", "csrc", "k_retrieve.hip")
 
 
@@ -263,7 +263,7 @@ def main():
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "traffic_detail": traffic,
-                     "kernel": "k_retrieve_mfma",
+                     "kernel": "k_retrieve_pair",
                      "bytes_per_launch": bytes_step / L,
                      "mfma_tflops": achieved_tflops,
                      "mfma_frac": achieved_tflops / MFMA_F16_PEAK_TFLOPS},

@@ -5,6 +5,12 @@
         `rocprofv3 --kernel-trace --stats` run (run_kernel_stats.csv),
         optionally only for kernels whose names contain one of the TEXTs
 
+    python -m cross_model_sparse_amd.profile_summary counters PASS_CSV... --kernel NAME \\
+        --command CMD [--command CMD ...] [--first K] [--skip S]
+        per-dispatch means of the counters of several `rocprofv3 --pmc` passes
+        over the same command, and the fraction of the kernel's active cycles
+        each texture-path, LDS, VALU and MFMA unit was busy or stalled
+
     python -m cross_model_sparse_amd.profile_summary traffic \\
         --fetch FETCH_CSV --write WRITE_CSV --copy-mib M --kernel NAME \\
         --fetch-command CMD --write-command CMD
@@ -55,16 +61,18 @@ def _dispatches(path: str, counter: str):
     return rows
 
 
-def _reference_window(rows):
+def _reference_window(rows, want: float):
     """(lo, hi): bench.py --copy-ref-mib runs the copy reference after the
-    capacity pass and before the first timed step, so it lies strictly between
-    the capacity pass's last gather (lo) and the step's first block-mass
-    launches (hi: the last block-mass dispatch before the step's first
-    retrieval launch)."""
-    first = next(i for i, r in enumerate(rows) if "k_retrieve_mfma" in r[1])
-    hi = max(i for i in range(first) if "k_block_mass" in rows[i][1])
-    lo = max(i for i in range(hi) if "k_gather" in rows[i][1])
-    return lo, hi
+    capacity pass and before the first timed step, so it lies between two
+    consecutive gather dispatches -- the capacity pass's last (lo) and the
+    step's first (hi) -- that precede the first retrieval launch, and it is
+    the only pair of them with a large elementwise dispatch in between."""
+    first = next(i for i, r in enumerate(rows) if "k_retrieve_" in r[1])
+    g = [i for i in range(first) if "k_gather" in rows[i][1]]
+    for lo, hi in zip(g, g[1:]):
+        if any("elementwise" in rows[k][1] and rows[k][2] > 0.25 * want for k in range(lo + 1, hi)):
+            return lo, hi
+    raise SystemExit("no copy-reference dispatch found between the capacity pass and the step")
 
 
 def _copy_reference(rows, mib: int):
@@ -72,7 +80,7 @@ def _copy_reference(rows, mib: int):
     dispatches in the reference window (the fill that creates the source reads
     nothing and is skipped by the > 1/4 size test in the fetch run)."""
     want = mib * 1024.0
-    lo, hi = _reference_window(rows)
+    lo, hi = _reference_window(rows, want)
     vals = [v for _, name, v in rows[lo + 1:hi]
             if "elementwise" in name and v > 0.25 * want]
     if not vals:
@@ -81,17 +89,21 @@ def _copy_reference(rows, mib: int):
     return vals[len(vals) // 2]
 
 
-def _kernel_mean(rows, kernel: str):
+def _kernel_mean(rows, kernel: str, want: float, first=None):
     """Mean counter value (KiB) and count of `kernel`'s dispatches after the
-    capacity pass (the timed steps' launches)."""
-    lo, _ = _reference_window(rows)
+    capacity pass (the timed steps' launches; only the first `first` of them
+    when given)."""
+    lo, _ = _reference_window(rows, want)
     vals = [v for _, name, v in rows[lo + 1:] if kernel in name]
+    if first:
+        vals = vals[:first]
     if not vals:
         raise SystemExit(f"no dispatch of {kernel} after the capacity pass")
     return sum(vals) / len(vals), len(vals)
 
 
-def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERNEL_SRC) -> str:
+def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERNEL_SRC,
+            first=None) -> str:
     fetch = _dispatches(fetch_csv, "FETCH_SIZE")
     write = _dispatches(write_csv, "WRITE_SIZE")
     want = mib * 1024.0
@@ -99,8 +111,8 @@ def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERN
     w_ref = _copy_reference(write, mib)
     f_scale = want / f_ref
     w_scale = want / w_ref
-    f_kib, nf = _kernel_mean(fetch, kernel)
-    w_kib, nw = _kernel_mean(write, kernel)
+    f_kib, nf = _kernel_mean(fetch, kernel, want, first)
+    w_kib, nw = _kernel_mean(write, kernel, want, first)
     fb = f_kib * 1024 * f_scale
     wb = w_kib * 1024 * w_scale
     src_hash = hashlib.sha256(open(source, "rb").read()).hexdigest()
@@ -128,6 +140,95 @@ def traffic(fetch_csv, write_csv, mib, kernel, fetch_cmd, write_cmd, source=KERN
     return "\n".join(lines) + "\n"
 
 
+# Unit counts of the MI355X (gfx950) used to turn summed counters into
+# fractions of the kernel's time: 8 XCDs (each reports its own
+# GRBM_GUI_ACTIVE), 256 active CUs, 4 SIMDs per CU.
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def _pmc_rows(path: str):
+    """{dispatch id: (kernel name, duration ns, {counter: value})}."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        if d not in out:
+            dur = int(r.get("End_Timestamp") or 0) - int(r.get("Start_Timestamp") or 0)
+            out[d] = (r["Kernel_Name"], dur, {})
+        out[d][2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def unit_fractions(c: dict) -> dict:
+    """Busy / stall fractions of the kernel's active time from one dispatch's
+    summed counters (only those whose counters are present).  Per-XCD active
+    cycles = GRBM_GUI_ACTIVE / 8; the formulas follow rocprofv3's derived
+    metrics (MfmaUtil, LdsUtil, LDSBankConflict, VALUBusy) with CU_NUM = 256
+    and SIMD_NUM = 1024, and divide the per-CU texture-path counters (summed
+    over instances) by 256 CUs."""
+    g = c.get("GRBM_GUI_ACTIVE")
+    if not g:
+        return {}
+    cyc = g / XCDS
+    per_cu = {"TA busy": "TA_TA_BUSY_sum", "TA address stalled by L1": "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+              "TD busy": "TD_TD_BUSY_sum", "TD stalled by L1": "TD_TC_STALL_sum",
+              "L1 pending-request stall": "TCP_PENDING_STALL_CYCLES_sum",
+              "L1 stalls TA data": "TCP_TCP_TA_DATA_STALL_CYCLES_sum",
+              "LDS active (LdsUtil)": "SQ_LDS_IDX_ACTIVE",
+              "LDS bank conflict": "SQ_LDS_BANK_CONFLICT",
+              "LDS data FIFO full": "SQ_LDS_DATA_FIFO_FULL",
+              "VALU busy (VALUBusy)": "SQ_ACTIVE_INST_VALU"}
+    f = {k: c[v] / (cyc * CUS) for k, v in per_cu.items() if v in c}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        f["MFMA busy (MfmaUtil)"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
+    return f
+
+
+def counters(csvs, kernel: str, commands, first=None, skip=0) -> str:
+    """Average of each counter over `kernel`'s dispatches (after skipping
+    `skip`, then the first `first`) in every pass, the unit fractions derived
+    from them, and the unit with the largest busy fraction."""
+    merged, fr, durs, n_disp, clk = {}, {}, [], [], []
+    for path in csvs:
+        disp = [v for _, v in sorted(_pmc_rows(path).items()) if kernel in v[0]][skip:]
+        disp = disp[:first] if first else disp
+        if not disp:
+            raise SystemExit(f"no dispatch of {kernel} in {path}")
+        n_disp.append(len(disp))
+        for name in disp[0][2]:
+            merged.setdefault(name, sum(d[2].get(name, 0.0) for d in disp) / len(disp))
+        per = [unit_fractions(d[2]) for d in disp]
+        for k in per[0]:
+            fr.setdefault(k, sum(p[k] for p in per) / len(per))
+        durs += [d[1] for d in disp]
+        clk += [d[2]["GRBM_GUI_ACTIVE"] / XCDS / d[1] for d in disp
+                if d[1] > 0 and "GRBM_GUI_ACTIVE" in d[2]]
+    lat = None
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in merged and merged.get("TCP_TCC_READ_REQ_sum"):
+        lat = merged["TCP_TCC_READ_REQ_LATENCY_sum"] / merged["TCP_TCC_READ_REQ_sum"]
+    out = [f"# rocprofv3 --pmc counters of {kernel}", "# REPO = repository root"]
+    out += [f"# pass {i + 1}: {cmd}" for i, cmd in enumerate(commands)]
+    out += [f"kernel: {kernel}",
+            f"dispatches per pass: {', '.join(map(str, n_disp))}"
+            + (f" (first {first} after skipping {skip})" if first else ""),
+            f"mean duration under counters: {sum(durs) / max(1, len(durs)) / 1e3:.1f} us"]
+    if clk:
+        out.append(f"active clock implied by GRBM_GUI_ACTIVE / 8 / duration: {sum(clk) / len(clk):.2f} GHz")
+    out += ["", "counter means per dispatch:"]
+    out += [f"  {k:36s} {v:16.4g}" for k, v in sorted(merged.items())]
+    if lat is not None:
+        out.append(f"  {'L1->L2 read latency (cycles)':36s} {lat:16.1f}")
+    if "TCC_HIT_sum" in merged and "TCC_MISS_sum" in merged:
+        h, m = merged["TCC_HIT_sum"], merged["TCC_MISS_sum"]
+        out.append(f"  {'L2 hit rate':36s} {h / max(1.0, h + m):16.3f}")
+    out += ["", "fraction of the kernel's active cycles:"]
+    out += [f"  {k:36s} {v:8.3f}" for k, v in sorted(fr.items(), key=lambda kv: -kv[1])]
+    busy = {k: v for k, v in fr.items() if "busy" in k or "active" in k}
+    if busy:
+        top = max(busy, key=busy.get)
+        out += ["", f"busiest unit: {top} ({busy[top]:.3f})"]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -147,12 +248,23 @@ def main(argv=None):
     t.add_argument("--source", default=KERNEL_SRC,
                    help="kernel source file whose SHA-256 the record carries "
                         "(default: the retrieval kernel's)")
+    t.add_argument("--first", type=int, default=None,
+                   help="average only the first FIRST dispatches after the capacity pass")
+    c = sub.add_parser("counters")
+    c.add_argument("csvs", nargs="+", help="pmc_counter_collection.csv of each pass")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", action="append", required=True,
+                   help="the command of each pass, in order (repeat per pass)")
+    c.add_argument("--first", type=int, default=None)
+    c.add_argument("--skip", type=int, default=0)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats(a.csv, a.command, a.top, a.match))
-    else:
+    elif a.cmd == "traffic":
         sys.stdout.write(traffic(a.fetch, a.write, a.copy_mib, a.kernel, a.fetch_command,
-                                 a.write_command, a.source))
+                                 a.write_command, a.source, a.first))
+    else:
+        sys.stdout.write(counters(a.csvs, a.kernel, a.command, a.first, a.skip))
 
 
 if __name__ == "__main__":

@@ -85,13 +85,87 @@ def test_bench_reports_traffic_only_for_the_measured_source(tmp_path, monkeypatc
 
 
 def test_committed_traffic_record_is_well_formed():
-    path = os.path.join(ROOT, "profiles", "k_retrieve_mfma_pair14b8b_bf16_N8192_traffic.txt")
+    bench = _bench()
+    path = bench.TRAFFIC_FILE
+    assert os.path.exists(path), path
     kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
               if line and not line.startswith("#"))
     fb, wb, hb = (float(kv[k]) for k in ("fetch_bytes_per_launch", "write_bytes_per_launch",
                                          "hbm_bytes_per_launch"))
     assert hb == pytest.approx(fb + wb, abs=2)
     assert len(kv["kernel_source_sha256"]) == 64
+    # the record is of the kernel the bench names for its roofline
+    assert kv["kernel"].startswith("k_retrieve_pair<")
+
+
+def test_traffic_with_all_layers_compressed_before_the_retrievals(tmp_path):
+    # the step compresses every layer, then retrieves every layer, then the
+    # warm order runs; only the step's first launches are averaged with first=2
+    def rows(ref, fill, k):
+        return [("k_block_mass<x>", 5.0), ("k_gather<x>", 7.0), ("k_block_mass<x>", 5.0),
+                ("k_gather<x>", 7.0),
+                ("vectorized_elementwise_kernel<FillFunctor>", fill),
+                ("vectorized_elementwise_kernel<MulFunctor>", ref),
+                ("vectorized_elementwise_kernel<MulFunctor>", ref),
+                ("k_block_mass<x>", 5.0), ("k_gather<x>", 7.0),
+                ("k_block_mass<x>", 5.0), ("k_gather<x>", 7.0),
+                ("k_retrieve_pair<true, 5, 2, false, false>", k),
+                ("k_retrieve_pair<true, 5, 2, false, false>", k),
+                ("k_block_mass<x>", 5.0), ("k_gather<x>", 7.0),
+                ("k_retrieve_pair<true, 5, 2, false, false>", 10 * k)]
+    _write(tmp_path / "f.csv", "FETCH_SIZE", rows(131072.0, 0.0, 1000.0))
+    _write(tmp_path / "w.csv", "WRITE_SIZE", rows(262144.0, 262144.0, 100.0))
+    rec = ps.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 256, "k_retrieve_pair",
+                     "a", "b", first=2)
+    kv = dict(line.split(": ", 1) for line in rec.splitlines() if not line.startswith("#"))
+    assert kv["dispatches_fetch_run"] == "2"
+    assert float(kv["fetch_bytes_per_launch"]) == pytest.approx(1000.0 * 1024 * 2)
+    assert float(kv["write_bytes_per_launch"]) == pytest.approx(100.0 * 1024)
+    rec = ps.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 256, "k_retrieve_pair",
+                     "a", "b")
+    kv = dict(line.split(": ", 1) for line in rec.splitlines() if not line.startswith("#"))
+    assert kv["dispatches_fetch_run"] == "3"
+
+
+def _write_pmc(path, dispatches):
+    """dispatches: [(name, duration ns, {counter: value})]"""
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+              "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for i, (name, dur, cs) in enumerate(dispatches, 1):
+            for c, v in cs.items():
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": c,
+                            "Counter_Value": v, "Start_Timestamp": 1000,
+                            "End_Timestamp": 1000 + dur})
+
+
+def test_counter_fractions_use_per_xcd_cycles_and_unit_counts(tmp_path):
+    # 100 us at 2 GHz: 200000 cycles per XCD, 1.6e6 summed over 8 XCDs
+    cyc = 200000.0
+    p1 = {"GRBM_GUI_ACTIVE": 8 * cyc, "TA_TA_BUSY_sum": 0.5 * cyc * 256,
+          "TD_TD_BUSY_sum": 0.25 * cyc * 256, "TCP_TCC_READ_REQ_LATENCY_sum": 4000.0,
+          "TCP_TCC_READ_REQ_sum": 10.0}
+    p2 = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.75 * cyc * 1024,
+          "SQ_LDS_IDX_ACTIVE": 0.125 * cyc * 256}
+    _write_pmc(tmp_path / "p1.csv", [("other", 5, {"GRBM_GUI_ACTIVE": 1.0}),
+                                     ("k_retrieve_pair<x>", 100000, p1)])
+    _write_pmc(tmp_path / "p2.csv", [("k_retrieve_pair<x>", 100000, p2)])
+    rec = ps.counters([str(tmp_path / "p1.csv"), str(tmp_path / "p2.csv")], "k_retrieve_pair",
+                      ["one", "two"])
+    frac = {}
+    for line in rec.split("fraction of the kernel's active cycles:")[1].splitlines():
+        parts = line.rsplit(None, 1)
+        if len(parts) == 2 and line.startswith("  "):
+            frac[parts[0].strip()] = float(parts[1])
+    assert frac["TA busy"] == pytest.approx(0.5, abs=1e-3)
+    assert frac["TD busy"] == pytest.approx(0.25, abs=1e-3)
+    assert frac["MFMA busy (MfmaUtil)"] == pytest.approx(0.75, abs=1e-3)
+    assert frac["LDS active (LdsUtil)"] == pytest.approx(0.125, abs=1e-3)
+    assert "busiest unit: MFMA busy (MfmaUtil)" in rec
+    assert "2.00 GHz" in rec and "400.0" in rec          # clock and L1->L2 latency
+    assert "# pass 2: two" in rec
 
 
 def test_traffic_of_a_kernel_that_also_runs_in_the_capacity_pass(tmp_path):
