@@ -132,6 +132,12 @@ __device__ __forceinline__ void dma16s(unsigned voff, const void* sbase, unsigne
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_base), "v"(voff), "s"(sgpr_ptr(sbase)) : "memory", "m0");
 }
+// The same copy with a base computed by scalar instructions only: no VALU
+// write of it to wait for (the static checks confirm it).
+__device__ __forceinline__ void dma16b(unsigned voff, const void* sbase, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -741,10 +747,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_mfma(
 //     16-key phases;
 //   * the V rows of the next chunk come straight into registers (eight 8-byte
 //     loads per lane, issued at the start of the phase before their use), so
-//     LDS holds only tile pairs and the two mixed-map buffers.
+//     LDS holds only tile pairs and the two mixed-map buffers;
+//   * the head mix reads its B operands out of the stage with the gfx950
+//     transposing LDS read (ds_read_b64_tr_b16), which hands each lane four
+//     sender heads of one (row, key) position, instead of reading head rows
+//     and transposing them in registers; for that, MFMA t of a chunk covers
+//     keys 4t..4t+3 of four rows, the mixed map is stored with the chunk's
+//     keys in the order 0,4,8,12,1,5,9,13,2,6,10,14,3,7,11,15, and V is
+//     loaded in the same order, so A.V pairs the same keys on both sides;
+//   * V and tile bases are computed by scalar instructions only, one 64-bit
+//     product per chunk and a row stride per load.
 // Pair P goes into stage P % 2 once the head mix of the previous occupant's
-// last chunk has passed a barrier: it is issued between the A.V MFMAs of
-// phase 2P-3 and waited for at the end of phase 2P-2.
+// last chunk has passed a barrier: its copies are issued between the A.V
+// MFMAs of phase 2P-3 (behind that phase's V loads) and waited for at the end
+// of phase 2P-2.
 
 // Split rows.  When a few long block rows would set the time of a launch (the
 // rows of a near-dense map run from 1 to T kept blocks), every row with more
@@ -814,16 +830,17 @@ __device__ bool split_item(const int32_t* __restrict__ row_ptr, int64_t nnzb, in
   return j < total;
 }
 
-// 8 bytes per lane from memory into a register pair: wave-uniform base and a
-// 32-bit per-lane byte offset, or a per-lane address.  The registers receive
-// the data asynchronously; they are read only after wait_vm_regs() has
-// retired the load.
-__device__ __forceinline__ void vld8s(u32x2& dst, unsigned voff, const void* sbase) {
-  asm volatile("s_nop 4\n\tglobal_load_dwordx2 %0, %1, %2"
-               : "=v"(dst) : "v"(voff), "s"(sgpr_ptr(sbase)) : "memory");
-}
+// 8 bytes per lane from memory into a register pair: a per-lane address, or
+// a wave-uniform base computed by scalar instructions (no VALU write of it to
+// wait for; the static checks confirm it) and a 32-bit per-lane byte offset.
+// The registers receive the data asynchronously; they are read only after
+// wait_vm_regs() has retired the load.
 __device__ __forceinline__ void vld8(u32x2& dst, const void* g) {
   asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(dst) : "v"(g) : "memory");
+}
+__device__ __forceinline__ void vld8b(u32x2& dst, unsigned voff, const void* sbase) {
+  asm volatile("global_load_dwordx2 %0, %1, %2"
+               : "=v"(dst) : "v"(voff), "s"(sbase) : "memory");
 }
 // s_waitcnt vmcnt(N) that the eight V registers depend on, so that no read of
 // them is scheduled above the wait.
@@ -904,44 +921,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   const int q = lane >> 4;
 
   // ---- head-mix role and W operands (as in k_retrieve_mfma) ----------------
+  // The head map's loads go first, so that their round trip overlaps those of
+  // row_ptr and of the first column; the conversion follows both.
   const int hm_mt = wave >> 2;
   const int rq = wave & 3;
-  u32x4 wop[NBOP][2];
+  float wraw[NBOP][2][8];
 #pragma unroll
   for (int b = 0; b < NBOP; ++b)
 #pragma unroll
-    for (int w = 0; w < Plan::nw(b); ++w) {
-      const int r = 16 * hm_mt + n;
-      const int c = Plan::chunk(b, q);
-      const int hf = Plan::half(b, w, q);
-      unsigned short hv[8];
+    for (int w = 0; w < Plan::nw(b); ++w)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        const int r = 16 * hm_mt + n;
+        const int c = Plan::chunk(b, q);
         const int s = 8 * c + j;
         const bool ok = c >= 0 && r < H_r && s < H_s;
         const float x = W[ok ? r * H_s + s : 0];
-        const float xv = ok ? x : 0.f;
-        if constexpr (kBF16) {
-          const unsigned short hi = bf16_bits(xv);
-          hv[j] = hf == 0 ? hi : bf16_bits(xv - bf16_to_f32(hi));
-        } else {
-          hv[j] = f32_to_f16(xv);
-        }
+        wraw[b][w][j] = ok ? x : 0.f;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wop[b][w][j] = (unsigned)hv[2 * j] | ((unsigned)hv[2 * j + 1] << 16);
-    }
-#pragma unroll
-  for (int b = 0; b < NBOP; ++b) asm volatile("" :: "v"(wop[b][0]));
-
-  f32x16 acc[NPAIR][4];
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[p][dt] = f32x16{};
-
-  const int rbeg = wave * RPW;
-  const int g = rbeg / G;
+  // ---- the row's kept blocks ------------------------------------------------
   int64_t kb = row_ptr[Ig], ke = row_ptr[Ig + 1];
   kb = kb < 0 ? 0 : (kb > nnzb ? nnzb : kb);
   ke = ke < kb ? kb : (ke > nnzb ? nnzb : ke);
@@ -983,12 +981,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     if constexpr (!kVar) return col_idx[k];
     else return page_of<kVar>(bt, block_table, k) >= 0 ? col_idx[k] : -1;
   };
+  // column of chunks 0 and 1 (one block: a block holds B/16 >= 2 chunks)
+  const int J0 = n_chunks > 0 ? col_of(0) : 0;
+  u32x4 wop[NBOP][2];
+#pragma unroll
+  for (int b = 0; b < NBOP; ++b)
+#pragma unroll
+    for (int w = 0; w < Plan::nw(b); ++w) {
+      const int hf = Plan::half(b, w, q);
+      unsigned short hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float xv = wraw[b][w][j];
+        if constexpr (kBF16) {
+          const unsigned short hi = bf16_bits(xv);
+          hv[j] = hf == 0 ? hi : bf16_bits(xv - bf16_to_f32(hi));
+        } else {
+          hv[j] = f32_to_f16(xv);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wop[b][w][j] = (unsigned)hv[2 * j] | ((unsigned)hv[2 * j + 1] << 16);
+    }
+#pragma unroll
+  for (int b = 0; b < NBOP; ++b) asm volatile("" :: "v"(wop[b][0]));
+
+  f32x16 acc[NPAIR][4];
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[p][dt] = f32x16{};
+
+  const int rbeg = wave * RPW;
+  const int g = rbeg / G;
 
   // Pair-stage layout: head slot hs holds 16 rows of 64 bytes; the four
-  // 16-byte quarters of row r sit in the order quarter ^ swz(r, hs / 8), so
-  // that one head-mix read (four sender groups x four rows x 32 bytes) spreads
-  // over all LDS banks instead of meeting itself 8 times on half of them.
-  auto swz = [](int r, int grp) { return (grp + (r >> 1)) & 3; };
+  // 16-byte quarters of each row sit in the order quarter ^ (hs % 4), so that
+  // a transposing head-mix read (four heads x four rows, 8 bytes each, per
+  // 16 lanes) meets every bank once.
+  auto swz = [](int hs) { return hs & 3; };
   // tile-pair copy d of this wavefront: head slot hs = wave + 8d; lane -> the
   // 16 bytes at LDS offset 16*lane of the slot, i.e. tile row lane/4 and
   // quarter (lane%4) ^ swz
@@ -998,7 +1029,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     const int hs = wave + kWaves * d;
     const int s = hs < H_s ? hs : H_s - 1;      // padding slots get a real head (zero weight)
     const int row = lane >> 2;
-    const int quarter = (lane & 3) ^ swz(row, hs >> 3);
+    const int quarter = (lane & 3) ^ swz(hs);
     head_off[d] = (unsigned)((s * tile + (int64_t)(sub * kRows + row) * B + quarter * 8) * 2);
   }
   const unsigned smem_lds = lds_addr(smem);
@@ -1009,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     const unsigned short* src;
     if constexpr (!kVar) src = vals + block_of(x) * H_s * tile + key_off(x);
     else src = vals + (page_ok(bt, pg) ? pg : 0) * H_s * tile + key_off(x);
-    dma16s(head_off[d], src, smem_lds + (P & 1) * kStage + (wave + kWaves * d) * kHeadPair);
+    dma16b(head_off[d], src, smem_lds + (P & 1) * kStage + (wave + kWaves * d) * kHeadPair);
   };
   auto pair_page = [&](int P) -> int64_t {
     if constexpr (!kVar) return 0;
@@ -1017,21 +1048,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   };
 
   // V rows of chunk x for this wavefront's KV head g, straight into registers:
-  // lane -> keys 8*(lane/32)+j (j = 0..7) of columns 4*(lane%32)..+3.  A
-  // chunk reaching past row N (only the last of a partial block) reads row
-  // N-1 for the missing keys; their mixed-map weights are zero.
-  const unsigned v_off = (unsigned)(((int64_t)(8 * (lane >> 5)) * ldV + g * kD + 4 * (lane & 31)) * 2);
+  // lane -> keys kperm(j) + 2*(lane/32) (j = 0..7) of columns 4*(lane%32)..+3.
+  // The keys of a chunk are taken in the order 0,4,8,12,1,5,9,13 | 2,6,10,
+  // 14,3,7,11,15 on both sides of A.V (the mixed map is stored in that
+  // order, see pack_row).  A chunk reaching past row N (only the last of a
+  // partial block) reads row N-1 for the missing keys; their mixed-map
+  // weights are zero.
+  auto kperm = [](int j) { return 4 * (j & 3) + (j >> 2); };
+  const unsigned v_off = (unsigned)(((int64_t)(2 * (lane >> 5)) * ldV + g * kD + 4 * (lane & 31)) * 2);
   const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
+  const int64_t ldV2 = ldV * 2;                  // bytes per V row
   u32x2 xv[8];
   auto issue_v = [&](int x, int J) {
     const int key0 = (col_ok(J) ? J : 0) * B + key_off(x);
     if (key0 + kCB <= N) {
+      // one 64-bit product per chunk, then a row stride per key
+      const char* vb = reinterpret_cast<const char*>(V + (int64_t)key0 * ldV);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vld8s(xv[j], v_off, V + (int64_t)(key0 + j) * ldV);
+      for (int j = 0; j < 8; ++j) vld8b(xv[j], v_off, vb + kperm(j) * ldV2);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int key = key0 + 8 * (lane >> 5) + j;
+        const int key = key0 + 2 * (lane >> 5) + kperm(j);
         vld8(xv[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
       }
     }
@@ -1041,12 +1079,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   const int hrow = 4 * rq + (n >> 2);
   const int hkq = n & 3;
   const int hm_off = hrow * 32 + (((hkq >> 1) ^ ((hrow >> 2) & 1)) * 16) + (hkq & 1) * 8;
-  auto key_ok = [&](int kvalid, int t) { return 4 * hkq + t < kvalid; };
+  // MFMA t of the head mix covers keys 4t + (position % 4): c[t] of this
+  // lane is key 4t + hkq
+  auto key_ok = [&](int kvalid, int t) { return 4 * t + hkq < kvalid; };
   // operand base of chunk x: its pair's stage and this lane's row; the
   // quarter (16-key half of the pair, 8-key half of that) is placed by
   // read_hm, which knows the sender group
   auto hm_base = [&](int x) -> const unsigned char* {
-    return smem + ((x >> 1) & 1) * kStage + hrow * 64;
+    return smem + ((x >> 1) & 1) * kStage;
   };
   auto pack_row = [&](unsigned char* dst, const f32x4 (&c)[4], int a, int kvalid) {
     const int rr = 16 * hm_mt + 4 * q + a;
@@ -1077,13 +1117,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
           c[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(wop[b][w]), as_f16x8(y[t]), c[t], 0, 0, 0);
       }
   };
-  // operands of group b for chunk half xh (x & 1): 4 keys x 8 sender heads
-  auto read_hm = [&](const unsigned char* st, int xh, int b, u32x2 (&x)[8]) {
+  // B operands of group b for chunk half xh (x & 1), straight from the
+  // stage with the transposing LDS read: for MFMA t, position n = 4r + e of
+  // this 16-lane group is (row 4rq + r, key 4t + e), and its 8 sender heads
+  // come from two reads in which source lane 4h + r points at keys 4t..4t+3
+  // of head h (then h + 4) of that row.
+  const int tr_h = (lane & 15) >> 2;
+  const int tr_row = 4 * rq + (lane & 3);
+  auto read_hm = [&](const unsigned char* st, int xh, int b, u32x4 (&y)[4]) {
     const int ch = Plan::chunk(b, q) < 0 ? 0 : Plan::chunk(b, q);
-    const int quarter = ((xh << 1) | (hkq >> 1)) ^ swz(hrow, ch);
-    const unsigned char* sp = st + quarter * 16 + (hkq & 1) * 8;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const u32x2*>(sp + (8 * ch + j) * kHeadPair);
+    for (int t = 0; t < 4; ++t) {
+      unsigned w[4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int slot = 8 * ch + 4 * hh + tr_h;
+        const int quarter = ((xh << 1) | (t >> 1)) ^ swz(slot);
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const unsigned char* pa = st + slot * kHeadPair + tr_row * 64 + quarter * 16 + (t & 1) * 8;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(pa));
+        const u32x2 u = __builtin_bit_cast(u32x2, v);
+        w[2 * hh] = u[0];
+        w[2 * hh + 1] = u[1];
+      }
+      y[t] = u32x4{w[0], w[1], w[2], w[3]};
+    }
   };
   // prologue form: head mix of chunk x into mixed-map buffer ab
   auto head_mix = [&](int x, int kvalid, int ab) {
@@ -1093,10 +1153,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < NBOP; ++b) {
-      u32x2 x8[8];
       u32x4 y[4];
-      read_hm(st, x & 1, b, x8);
-      transpose8x4(x8, y);
+      read_hm(st, x & 1, b, y);
       hm_mfmas(y, b, c);
     }
     unsigned char* dst = smem + kAhatOff + ab * kAhatBuf + hm_off;
@@ -1117,15 +1175,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     f32x4 c[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x2 x[8];
-    read_hm(st, x1 & 1, 0, x);
+    u32x4 y[4];
+    read_hm(st, x1 & 1, 0, y);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < NBOP; ++b) {
-      u32x4 y[4];
-      transpose8x4(x, y);
-      if (b + 1 < NBOP) read_hm(st, x1 & 1, b + 1, x);
+      u32x4 yn[4];
+      if (b + 1 < NBOP) read_hm(st, x1 & 1, b + 1, yn);
       hm_mfmas(y, b, c);
+      if (b + 1 < NBOP) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] = yn[t];
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
@@ -1156,15 +1217,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   int J1 = 0;                                    // column of chunk u+1
   int64_t pg_next = 0;                           // table page of the next pair to copy
   if (n_chunks > 0) {
-    const int J0 = col_of(0);
-    J1 = col_of(1);
-    issue_v(0, J0);
+    J1 = J0;
+    // pair 0 needs only row_ptr, V(0) the first column: pair 0 goes first, and
+    // V(0) sits between the pairs so that one wait covers pair 0 and V(0)
     const int64_t pg0 = pair_page(0), pg1 = pair_page(1);
 #pragma unroll
     for (int d = 0; d < NCH; ++d) issue_pair(0, pg0, d);
+    issue_v(0, J0);
 #pragma unroll
     for (int d = 0; d < NCH; ++d) issue_pair(1, pg1, d);
-    wait_vm_regs<NCH>(xv);                       // V(0) and pair 0 landed
+    wait_vm_regs<NCH>(xv);                       // pair 0 and V(0) landed (pair 1 in flight)
     lds_barrier();
     head_mix(0, kvalid_of(0, J0), 0);
     lds_barrier();
@@ -1185,14 +1247,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     transpose8x4(xv, vt);                        // V(u)
     issue_v(u + 1, J1);                          // V(u+1)
     // odd phase: pair (u+3)/2 into the stage whose last chunk was head-mixed
-    // in the previous phase, right behind V(u+1): loads return in issue
-    // order, so V goes first, and the pair gets two whole phases
+    // in the previous phase, its copies spread over the A.V steps behind
+    // V(u+1) (loads return in issue order, so V goes first and the copies do
+    // not queue ahead of it); the pair has until the end of the next phase
     const int P = (u + 3) >> 1;
-    if constexpr (kOdd) {
+    auto step_copy = [&](int st) {
+      if constexpr (kOdd) {
 #pragma unroll
-      for (int d = 0; d < NCH; ++d) issue_pair(P, pg_next, d);
-    }
-    auto step_copy = [&](int) {};
+        for (int d = 0; d < NCH; ++d)
+          if (d * kSteps / NCH == st) issue_pair(P, pg_next, d);
+      }
+    };
     compute(u + 1, u + 1 < n_chunks ? kvalid_of(u + 1, J1) : 0, (u + 1) & 1, u & 1, vt, step_copy);
     if constexpr (kOdd) {
       wait_vm_regs<NCH>(xv);                     // V(u+1) landed (this phase's pair in flight)

@@ -13,8 +13,8 @@ programmer's job:
                control-flow graph, takes uniform branches whose condition is a
                known constant, and assumes a full exec mask);
   valu_sgpr    no vector-memory instruction reads an SGPR fewer than 5 wait
-               states after a VALU instruction (v_readfirstlane, v_readlane)
-               wrote it;
+               states after a VALU instruction wrote it (lane reads, compare
+               masks, carry outs);
   m0_dma       no LDS DMA directly follows the SALU write of M0 it uses;
   m0_live      no instruction outside the copy statements reads M0 while the
                last M0 write before it (in program order) is a copy
@@ -208,18 +208,46 @@ def _inflight(body, max_states=64):
     return sorted(bad.items())
 
 
+# VALU instructions whose second operand is a scalar destination (carry out,
+# division scale flag): the VOP3b forms.
+_VOP3B = re.compile(r"^v_(add|sub|subrev|addc|subb|subbrev)_co_|^v_div_scale_|^v_mad_[iu]64_[iu]32")
+
+
+def _sgprs(tok: str) -> frozenset:
+    if tok == "vcc":
+        return frozenset({106, 107})
+    m = re.match(r"s\[(\d+):(\d+)\]$", tok)
+    if m:
+        return frozenset(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return frozenset({int(m.group(1))}) if m else frozenset()
+
+
+def _valu_sgpr_dests(s: str) -> frozenset:
+    """SGPRs a VALU instruction writes: lane reads, compare masks, carries."""
+    parts = s.replace(",", " ").split()
+    op, ops = parts[0], parts[1:]
+    if not op.startswith("v_") or not ops:
+        return frozenset()
+    if op.startswith(("v_readfirstlane", "v_readlane")) or (op.startswith("v_cmp") and not op.startswith("v_cmpx")):
+        return _sgprs(ops[0])
+    if _VOP3B.match(op) and len(ops) > 1:
+        return _sgprs(ops[1])
+    return frozenset()
+
+
 def _linear_hazards(body):
     insts = [s for _, s in body if not s.startswith(".")]
     lines = [ln for ln, s in body if not s.startswith(".")]
     valu_sgpr, m0 = [], []
     for i, s in enumerate(insts):
-        m = re.match(r"v_read(first)?lane_b32 s(\d+)", s)
-        if m:
-            n, ws = int(m.group(2)), 0
+        dst = _valu_sgpr_dests(s)
+        if dst:
+            ws = 0
             for j in range(i + 1, min(len(insts), i + 8)):
                 x = insts[j]
                 if VMEM.match(x.split()[0]) and ws < 5:
-                    if any(lo <= n <= hi for lo, hi in _sgpr_ranges(x)):
+                    if any(n in dst for lo, hi in _sgpr_ranges(x) for n in range(lo, hi + 1)):
                         valu_sgpr.append((lines[j], x))
                 k = re.match(r"s_nop (\d+)", x)
                 ws += int(k.group(1)) + 1 if k else 1
@@ -299,7 +327,7 @@ def main(argv):
     with tempfile.TemporaryDirectory() as td:
         asm = Path(td) / "k.s"
         compile_to_asm(src, asm)
-        res = check_asm(str(asm))
+        res = check_asm(str(asm), pattern="k_")
     bad = 0
     for name, r in sorted(res.items()):
         n = (r["scratch"] + len(r["inflight"]) + len(r["valu_sgpr"]) + len(r["m0_dma"])

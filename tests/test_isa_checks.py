@@ -91,6 +91,24 @@ def test_checker_flags_m0_live_across_a_copy(tmp_path):
     assert [s for _, s in r["m0_live"]] == ["v_movrel_b32_e32 v1, v2"]
 
 
+def test_checker_flags_vmem_after_any_valu_sgpr_write(tmp_path):
+    # a compare mask and a carry out are VALU writes of SGPRs too
+    text = PLANTED.replace("\tv_readfirstlane_b32 s8, v10\n\tv_readfirstlane_b32 s9, v11\n",
+                           "\tv_cmp_gt_i32_e64 s[8:9], v10, v11\n")
+    r = _check_text(tmp_path, text)
+    assert [s for _, s in r["valu_sgpr"]] == ["global_load_dwordx2 v[20:21], v30, s[8:9]",
+                                              "global_load_lds_dwordx4 v31, s[8:9]"]
+    text = PLANTED.replace("\tv_readfirstlane_b32 s8, v10\n\tv_readfirstlane_b32 s9, v11\n",
+                           "\tv_mad_u64_u32 v[2:3], s[8:9], s10, v4, 0\n")
+    r = _check_text(tmp_path, text)
+    assert len(r["valu_sgpr"]) == 2
+    # a VALU write of another SGPR, or a scalar write, is not a hazard
+    text = PLANTED.replace("\tv_readfirstlane_b32 s8, v10\n\tv_readfirstlane_b32 s9, v11\n",
+                           "\tv_cmp_gt_i32_e64 s[20:21], v10, v11\n\ts_add_u32 s8, s8, 64\n")
+    r = _check_text(tmp_path, text)
+    assert not r["valu_sgpr"]
+
+
 def test_checker_accepts_the_fixed_forms(tmp_path):
     r = _check_text(tmp_path, CLEAN)
     assert r["scratch"] == 0 and not r["valu_sgpr"] and not r["m0_dma"] and not r["inflight"]
