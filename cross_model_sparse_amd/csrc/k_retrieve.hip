@@ -245,20 +245,28 @@ __device__ __forceinline__ int64_t page_of(const Batch& bt, const int32_t* __res
 // ---------------------------------------------------------------------------
 
 // Work item of workgroup b: blocks of RG consecutive block rows are dealt to
-// the 8 XCDs in turn (workgroups go to XCDs round-robin by index), so rows
-// that share band columns share an L2; within an XCD rows are taken from the
-// last to the first.
+// the 8 XCDs (workgroups go to XCDs round-robin by index, whatever their
+// load), so rows that share band columns share an L2; the deal runs forward
+// and backward in turn over the XCDs, so that rows of unequal length even out
+// across them; within an XCD rows are taken from the last to the first.
 __device__ __forceinline__ int item_of(int b, int subs, int T, int RG, int* I, int* sub) {
   const int xcd = b & 7;
   const int local = b >> 3;
   const int lrow = local / subs;                 // row index within this XCD's list
-  const int grp = (lrow / RG) * 8 + xcd;         // global row group
+  const int rnd = lrow / RG;                     // deal round
+  const int grp = rnd * 8 + ((rnd & 1) ? 7 - xcd : xcd);   // global row group
   const int row_slot = grp * RG + lrow % RG;
   if (row_slot >= T) return 0;
   *I = T - 1 - row_slot;
   *sub = local % subs;
   return 1;
 }
+
+// Block rows per group dealt to one XCD.  Groups of 16 rows (a sixteenth of
+// the rows) left the long-context layer, whose rows keep 1 to 66 blocks, with
+// one XCD doing four times the work of another; groups of R/64 rows dealt in
+// alternating order even that out and lose nothing on the other layers.
+inline int row_group(int R) { return R / 64 > 1 ? R / 64 : 1; }
 
 // Head-mix K-step plan.  Sender heads come in NCH chunks of 8.
 //  fp16: operand b covers chunks 4b..4b+3 (lane group q -> chunk 4b+q), W in fp16.
@@ -1659,7 +1667,7 @@ int retrieve_impl(const int32_t* row_ptr, const int32_t* col_idx, const void* va
     return launch_split(row_ptr, col_idx, vals, nnzb, dt, H_s, N, B, W, H_r, V, H_kv, ldV, O, ldO,
                         workspace, st);
   if (retrieve_uses_mfma(dt, H_s, B, H_r, H_kv, d, vals, V, ldV, O, ldO)) {
-    const int RG = std::max(1, R / 16);
+    const int RG = row_group(R);
     const int groups = (R + RG - 1) / RG;
     const int rows_per_xcd = ((groups + 7) / 8) * RG;
     const dim3 grid(rows_per_xcd * 8 * (B / kRows));
@@ -1718,7 +1726,7 @@ int launch_retrieve_multi(const int32_t* row_ptr, const int32_t* col_idx, const 
     max_rpw = std::max(max_rpw, H_r[i] / 8);
   }
   const int R = blocks_of(N, B);
-  const int RG = std::max(1, R / 16);
+  const int RG = row_group(R);
   const int groups = (R + RG - 1) / RG;
   const int rows_per_xcd = ((groups + 7) / 8) * RG;
   const dim3 grid(rows_per_xcd * 8 * (B / kRows) * n_recv);
