@@ -1066,22 +1066,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   const unsigned v_off = (unsigned)(((int64_t)(2 * (lane >> 5)) * ldV + g * kD + 4 * (lane & 31)) * 2);
   const unsigned short* vlane = V + (int64_t)g * kD + 4 * (lane & 31);
   const int64_t ldV2 = ldV * 2;                  // bytes per V row
-  u32x2 xv[8];
-  auto issue_v = [&](int x, int J) {
+  u32x2 xv[2][8];                                // raw V of the even and the odd chunks
+  // loads j0 <= j < j1 of V(x) into xd
+  auto issue_v_part = [&](int x, int J, u32x2 (&xd)[8], int j0, int j1) {
     const int key0 = (col_ok(J) ? J : 0) * B + key_off(x);
     if (key0 + kCB <= N) {
       // one 64-bit product per chunk, then a row stride per key
       const char* vb = reinterpret_cast<const char*>(V + (int64_t)key0 * ldV);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vld8b(xv[j], v_off, vb + kperm(j) * ldV2);
+      for (int j = 0; j < 8; ++j)
+        if (j >= j0 && j < j1) vld8b(xd[j], v_off, vb + kperm(j) * ldV2);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = key0 + 2 * (lane >> 5) + kperm(j);
-        vld8(xv[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
+        if (j >= j0 && j < j1) vld8(xd[j], vlane + (int64_t)(key < N ? key : N - 1) * ldV);
       }
     }
   };
+  auto issue_v = [&](int x, int J, u32x2 (&xd)[8]) { issue_v_part(x, J, xd, 0, 8); };
 
   // ---- head mix ---------------------------------------------------------------
   const int hrow = 4 * rq + (n >> 2);
@@ -1175,10 +1178,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
   constexpr int kSteps = NPAIR * NPL;            // A.V steps that can carry a copy
 
   // One phase: head-mix operand reads and MFMAs of chunk x1 (next operand's
-  // transpose between them), then the A.V MFMAs of the current chunk with the
-  // packing of the head-mix result and the phase's tile-pair copies between
-  // them.
-  auto compute = [&](int x1, int kvalid, int ab_hm, int ab_av, const u32x4 (&vt)[4], auto&& step_copy) {
+  // reads between them), the current chunk's V operands (prep_v), then its
+  // A.V MFMAs with the packing of the head-mix result and the phase's loads
+  // (step_copy) between them.
+  auto compute = [&](int x1, int kvalid, int ab_hm, int ab_av, auto&& prep_v, auto&& step_copy) {
     const unsigned char* st = hm_base(x1);
     f32x4 c[4];
 #pragma unroll
@@ -1197,6 +1200,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    u32x4 vt[4];
+    prep_v(vt);
     const unsigned char* asrc = smem + kAhatOff + ab_av * kAhatBuf + a_off;
     unsigned char* dst = smem + kAhatOff + ab_hm * kAhatBuf + hm_off;
 #pragma unroll
@@ -1231,47 +1236,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     const int64_t pg0 = pair_page(0), pg1 = pair_page(1);
 #pragma unroll
     for (int d = 0; d < NCH; ++d) issue_pair(0, pg0, d);
-    issue_v(0, J0);
+    issue_v(0, J0, xv[0]);
 #pragma unroll
     for (int d = 0; d < NCH; ++d) issue_pair(1, pg1, d);
-    wait_vm_regs<NCH>(xv);                       // pair 0 and V(0) landed (pair 1 in flight)
+    wait_vm_regs<NCH>(xv[0]);                    // pair 0 and V(0) landed (pair 1 in flight)
     lds_barrier();
     head_mix(0, kvalid_of(0, J0), 0);
     lds_barrier();
     pg_next = pair_page(2);
   }
   // Two phases per iteration (n_chunks is even for B >= 32), so that which
-  // phases copy a pair and how many copies each wait leaves in flight are
-  // fixed in the code: the even phase copies nothing and waits for
-  // everything, the odd phase copies pair (u+3)/2 and waits for all but those
-  // NCH copies.
+  // loads each phase issues and how many each wait leaves in flight are
+  // fixed in the code.  Phase u waits for V(u) and transposes it after its
+  // head mix, right before its A.V MFMAs.
+  // - Even phase: no tile copies.  V(u+1) is loaded in parts, one behind the
+  //   transpose and one behind each A.V step, so that the eight wavefronts'
+  //   V loads do not reach the texture path at once and stall their issue.
+  //   At its end it waits only for the pair copied in the previous phase.
+  // - Odd phase: V(u+1) at its start, then pair (u+3)/2 into the stage whose
+  //   last chunk was head-mixed in the previous phase, its copies spread over
+  //   the A.V steps (loads return in issue order, so V goes first and the
+  //   copies do not queue ahead of it); the pair has until the end of the
+  //   next phase.  It ends with no wait: the next head mix reads the second
+  //   chunk of a pair that has landed, and V(u+1) stays in flight across the
+  //   loop's back edge (the static checks confirm that no instruction reads
+  //   or writes those registers before the wait that retires them).
   auto phase = [&](int u, auto odd_tag) {
     constexpr bool kOdd = decltype(odd_tag)::value;
     const int64_t kn = block_of(u + 2);          // column of chunk u+2: used after the barrier
     const int Jn_col = col_idx[kn];
     int64_t pg_J = 0;
     if constexpr (kVar) pg_J = page_raw<kVar>(block_table, col_idx, kn);
-    u32x4 vt[4];
-    transpose8x4(xv, vt);                        // V(u)
-    issue_v(u + 1, J1);                          // V(u+1)
-    // odd phase: pair (u+3)/2 into the stage whose last chunk was head-mixed
-    // in the previous phase, its copies spread over the A.V steps behind
-    // V(u+1) (loads return in issue order, so V goes first and the copies do
-    // not queue ahead of it); the pair has until the end of the next phase
+    if constexpr (kOdd) issue_v(u + 1, J1, xv[0]);
     const int P = (u + 3) >> 1;
     auto step_copy = [&](int st) {
-      if constexpr (kOdd) {
+      if constexpr (!kOdd) {
+        issue_v_part(u + 1, J1, xv[1], (st + 1) * 8 / (kSteps + 1), (st + 2) * 8 / (kSteps + 1));
+      } else {
 #pragma unroll
         for (int d = 0; d < NCH; ++d)
           if (d * kSteps / NCH == st) issue_pair(P, pg_next, d);
       }
     };
-    compute(u + 1, u + 1 < n_chunks ? kvalid_of(u + 1, J1) : 0, (u + 1) & 1, u & 1, vt, step_copy);
+    auto prep_v = [&](u32x4 (&vt)[4]) {
+      if constexpr (kOdd) {
+        wait_vm_regs<8>(xv[1]);                  // V(u): only V(u+1) was issued after it
+        transpose8x4(xv[1], vt);
+      } else {
+        wait_vm_regs<NCH>(xv[0]);                // V(u): the copies of a pair were issued after it
+        transpose8x4(xv[0], vt);
+        issue_v_part(u + 1, J1, xv[1], 0, 8 / (kSteps + 1));
+      }
+    };
+    compute(u + 1, u + 1 < n_chunks ? kvalid_of(u + 1, J1) : 0, (u + 1) & 1, u & 1, prep_v, step_copy);
     if constexpr (kOdd) {
-      wait_vm_regs<NCH>(xv);                     // V(u+1) landed (this phase's pair in flight)
       if constexpr (kVar) pg_next = pair_page(P + 1);
     } else {
-      wait_vm_regs<0>(xv);                       // V(u+1) and the pair copied last phase
+      wait_vm<8>();                              // the pair copied last phase (V(u+1) stays in flight)
     }
     lds_barrier();
     J1 = (!kVar || page_ok(bt, pg_J)) ? Jn_col : -1;
@@ -1280,7 +1301,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_retrieve_pair(
     phase(u, std::false_type{});
     phase(u + 1, std::true_type{});
   }
-  wait_vm<0>();
+  wait_vm_regs<0>(xv[0]);                        // no V load in flight past the loop
+  wait_vm_regs<0>(xv[1]);
   lds_barrier();
 
   // ---- a part of a split row: fp32 partials, 16 bytes (4 head-dim columns) per lane
