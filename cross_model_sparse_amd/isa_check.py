@@ -158,7 +158,17 @@ def _decode(s):
 
 
 def _inflight(body, max_states=64):
-    """Lines touching the destination VGPRs of outstanding vector loads."""
+    """Lines touching the destination VGPRs of outstanding vector loads.
+
+    The walk follows every path of the kernel's control-flow graph (scalar
+    branches on a known vcc are resolved) to a fixed point.  A state holds,
+    for each outstanding load that writes VGPRs, its registers and how many
+    vector-memory operations were issued after it (capped at 64: any
+    vmcnt(n) retires such a load, as n <= 63); loads into LDS only add to
+    those counts.  That is exactly what `s_waitcnt vmcnt(n)` needs (it
+    retires every load with n or more operations issued after it), and it
+    keeps the number of states small where copies of varying count are in
+    flight."""
     order, blocks, succ = _blocks(body)
     code = {b: [(ln, s, _decode(s)) for ln, s in blocks[b]] for b in order}
     states = {b: set() for b in order}
@@ -184,14 +194,16 @@ def _inflight(body, max_states=64):
                                 if a & set(range(*map(int, k[2:-1].split(":")))):
                                     consts.pop(k, None)
                 if kind == "wait":
-                    fifo = fifo[len(fifo) - x:] if len(fifo) > x else fifo
+                    fifo = [(d, n) for d, n in fifo if n < x]
                 elif kind == "vmem":
-                    for d in fifo:
+                    for d, _ in fifo:
                         if y & d or x & d:
                             bad.setdefault(ln, s)
-                    fifo.append(x)
+                    fifo = [(d, min(n + 1, 64)) for d, n in fifo]
+                    if x:
+                        fifo.append((x, 0))
                 elif kind == "use" and fifo:
-                    for d in fifo:
+                    for d, _ in fifo:
                         if x & d:
                             bad.setdefault(ln, s)
             out = (tuple(fifo), frozenset(consts.items()))
@@ -202,9 +214,16 @@ def _inflight(body, max_states=64):
             elif last.startswith("s_cbranch_vccz") and "vcc" in consts:
                 nbs = nbs[1:] if consts["vcc"] else nbs[:1]
             for nb in nbs:
-                if nb in states and out not in states[nb] and len(states[nb]) < max_states:
-                    states[nb].add(out)
-                    work.append(nb)
+                if nb in states and out not in states[nb]:
+                    if len(states[nb]) < max_states:
+                        states[nb].add(out)
+                        work.append(nb)
+                    elif blocks[nb]:
+                        # a state left unexplored would make the walk unsound:
+                        # report it rather than pass the kernel
+                        ln0 = blocks[nb][0][0]
+                        bad.setdefault(ln0, f"(walk incomplete: more than {max_states} states) "
+                                            + blocks[nb][0][1])
     return sorted(bad.items())
 
 

@@ -109,6 +109,41 @@ def test_checker_flags_vmem_after_any_valu_sgpr_write(tmp_path):
     assert not r["valu_sgpr"]
 
 
+TWO_PATHS = """
+_Zk_retrieve_mfma_demo:
+\ts_cbranch_scc1 .LBB0_2
+\tglobal_load_dwordx2 v[20:21], v30, s[8:9]
+.LBB0_2:
+\tv_add_u32_e32 v40, v22, v41
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+"""
+
+
+def test_checker_reports_a_walk_it_cannot_finish():
+    # two paths meet with different loads in flight: two states at the join.
+    # With room for one, the walk cannot finish and says so instead of
+    # passing the kernel; with room for two it finishes and finds nothing.
+    lines = TWO_PATHS.strip("\n").split("\n")
+    body = isa_check._functions(lines)["_Zk_retrieve_mfma_demo"]
+    r = isa_check._inflight(body, max_states=1)
+    assert r and all("walk incomplete" in s for _, s in r)
+    assert isa_check._inflight(body, max_states=2) == []
+
+
+def test_checker_counts_copies_into_lds_toward_waits(tmp_path):
+    # a register load, then two copies into LDS: vmcnt(2) retires the load,
+    # vmcnt(3) does not
+    text = CLEAN.replace("\ts_waitcnt vmcnt(1)\n",
+                         "\tglobal_load_lds_dwordx4 v31, s[8:9]\n\ts_waitcnt vmcnt(3)\n")
+    r = _check_text(tmp_path, text)
+    assert [s for _, s in r["inflight"]] == ["v_add_u32_e32 v40, v20, v41"]
+    text = CLEAN.replace("\ts_waitcnt vmcnt(1)\n",
+                         "\tglobal_load_lds_dwordx4 v31, s[8:9]\n\ts_waitcnt vmcnt(2)\n")
+    r = _check_text(tmp_path, text)
+    assert not r["inflight"]
+
+
 def test_checker_accepts_the_fixed_forms(tmp_path):
     r = _check_text(tmp_path, CLEAN)
     assert r["scratch"] == 0 and not r["valu_sgpr"] and not r["m0_dma"] and not r["inflight"]
